@@ -1,0 +1,12 @@
+"""fp64 CPU oracle (test infrastructure only; never imported by the product path)."""
+
+from .attention import (  # noqa: F401
+    causal_attention,
+    causal_attention_bruteforce,
+    causal_flops,
+    kv_head_of,
+    softmax_scale,
+    unmasked_pairs,
+    visible,
+    zigzag_positions,
+)

@@ -1,0 +1,243 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` takes an oracle namespace ``o`` (attributes ``causal_attention``,
+``causal_attention_bruteforce``, ``zigzag_positions``, ``unmasked_pairs``,
+``kv_head_of``) and raises AssertionError when the implementation breaks the pin. The
+same pins run against deliberately broken copies in test_oracle_mutants.py, which
+shows that a plausible mistake anywhere in the oracle trips at least one of them.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# -- the zigzag map ----------------------------------------------------------------------
+
+def pin_zigzag_golden(o):
+    """Chunk ownership of the workloads' shards (zigzag_ownership.json)."""
+    for c in _load("zigzag_ownership.json")["cases"]:
+        S, D, r = c["S_total"], c["D"], c["rank"]
+        C = S // (2 * D)
+        lo, hi = c["chunks"]
+        pos = np.asarray(o.zigzag_positions(S, D, r))
+        assert pos.shape == (2 * C,), (c, pos.shape)
+        assert np.array_equal(pos[:C], np.arange(lo * C, (lo + 1) * C)), c
+        assert np.array_equal(pos[C:], np.arange(hi * C, (hi + 1) * C)), c
+
+
+def pin_zigzag_permutation(o):
+    """Over all ranks the map is a permutation of [0, S_total); D = 1 is the identity."""
+    for S, D in [(8, 1), (24, 2), (48, 3), (64, 4), (512, 4), (4096, 8), (1040, 8)]:
+        allpos = np.concatenate([np.asarray(o.zigzag_positions(S, D, r)) for r in range(D)])
+        assert np.array_equal(np.sort(allpos), np.arange(S)), (S, D)
+        for r in range(D):
+            pos = np.asarray(o.zigzag_positions(S, D, r))
+            assert np.all(np.diff(pos) > 0), (S, D, r)
+    assert np.array_equal(np.asarray(o.zigzag_positions(96, 1, 0)), np.arange(96))
+
+
+def pin_pairs_closed_form(o):
+    """Every rank sees C * (S_total + 1) visible (query, key) pairs per (batch, head).
+
+    Closed form: chunks c and 2D-1-c contribute (c*C^2 + C(C+1)/2) and
+    ((2D-1-c)*C^2 + C(C+1)/2); their sum is (2D-1)*C^2 + C^2 + C = C*(S_total + 1).
+    """
+    for S, D in [(512, 4), (32768, 8), (65536, 4), (131072, 1), (262144, 8), (120, 3), (14, 7)]:
+        C = S // (2 * D)
+        for r in range(D):
+            assert int(o.unmasked_pairs(S, D, r)) == C * (S + 1), (S, D, r)
+
+
+def pin_gqa_ownership(o):
+    """The lesson page's degree-4 split of 24 query heads over 4 KV heads."""
+    g = _load("gqa_head_ownership.json")
+    Hq, Hkv, deg = g["Hq"], g["Hkv"], g["degree"]
+    per = Hq // deg
+    assert per == g["query_heads_per_rank"]
+    assert Hkv * g["dh"] == g["kv_proj_width"]
+    for r in range(deg):
+        owned = {o.kv_head_of(h, Hq, Hkv) for h in range(r * per, (r + 1) * per)}
+        assert len(owned) == g["kv_heads_per_rank"], (r, owned)
+    used = [o.kv_head_of(h, Hq, Hkv) for h in range(Hq)]
+    assert sorted(set(used)) == list(range(Hkv))
+
+
+# -- the attention ---------------------------------------------------------------------
+
+TINY = [  # (B, S_total, D, rank, Hq, Hkv, dh)
+    (1, 8, 1, 0, 1, 1, 4),
+    (1, 16, 2, 1, 2, 1, 4),
+    (2, 24, 3, 0, 3, 3, 3),
+    (1, 24, 3, 2, 4, 2, 5),
+    (1, 32, 4, 1, 4, 1, 8),
+]
+
+
+def _tiny_inputs(case, seed):
+    B, S, D, r, Hq, Hkv, dh = case
+    q = _rand((B, S // D, Hq, dh), seed)
+    k = _rand((B, S, Hkv, dh), seed + 1)
+    v = _rand((B, S, Hkv, dh), seed + 2)
+    return q, k, v
+
+
+def pin_bruteforce(o):
+    """Blocked matrix form == scalar triple loop, with blocks smaller than a chunk."""
+    for n, case in enumerate(TINY):
+        q, k, v = _tiny_inputs(case, 10 + n)
+        D, r = case[2], case[3]
+        out_b, lse_b = o.causal_attention(q, k, v, D, r, block=3)
+        out_r, lse_r = o.causal_attention_bruteforce(q, k, v, D, r)
+        assert np.allclose(out_b, out_r, rtol=0, atol=1e-12), case
+        assert np.allclose(lse_b, lse_r, rtol=0, atol=1e-12), case
+
+
+def pin_sdpa_one_rank(o):
+    """D = 1 (Ulysses head subset) equals PyTorch's causal SDPA in fp64 on the CPU."""
+    for B, S, Hq, Hkv, dh, seed in [(1, 40, 2, 2, 8, 1), (2, 33 * 2, 6, 2, 16, 2), (1, 128, 4, 1, 32, 3)]:
+        q = _rand((B, S, Hq, dh), seed)
+        k = _rand((B, S, Hkv, dh), seed + 1)
+        v = _rand((B, S, Hkv, dh), seed + 2)
+        out, lse = o.causal_attention(q, k, v, 1, 0)
+        grp = Hq // Hkv
+        tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+        tk = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(grp, dim=1)
+        tv = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(grp, dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+        ref = ref.permute(0, 2, 1, 3).numpy()
+        assert np.allclose(out, ref, rtol=0, atol=1e-12), (B, S, Hq, Hkv, dh)
+        s = torch.einsum("bhid,bhjd->bhij", tq, tk) / math.sqrt(dh)
+        s = s.masked_fill(torch.triu(torch.ones(S, S, dtype=torch.bool), 1), float("-inf"))
+        assert np.allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def pin_concatenation(o):
+    """Scattering every rank's rows by global position rebuilds the unsharded result."""
+    for B, S, D, Hq, Hkv, dh, seed in [(1, 48, 3, 2, 1, 4, 5), (1, 64, 4, 4, 2, 8, 6), (2, 32, 2, 1, 1, 4, 7)]:
+        qf = _rand((B, S, Hq, dh), seed)
+        k = _rand((B, S, Hkv, dh), seed + 1)
+        v = _rand((B, S, Hkv, dh), seed + 2)
+        full_out, full_lse = o.causal_attention(qf, k, v, 1, 0)
+        got_out = np.full_like(full_out, np.nan)
+        got_lse = np.full_like(full_lse, np.nan)
+        for r in range(D):
+            pos = np.asarray(o.zigzag_positions(S, D, r))
+            out, lse = o.causal_attention(qf[:, pos], k, v, D, r)
+            got_out[:, pos] = out
+            got_lse[:, :, pos] = lse
+        assert np.allclose(got_out, full_out, rtol=0, atol=1e-12), (S, D)
+        assert np.allclose(got_lse, full_lse, rtol=0, atol=1e-12), (S, D)
+
+
+def pin_probabilities(o):
+    """One-hot values expose the softmax matrix: rows sum to 1, zero exactly past the
+    query's global position, positive up to it, and equal exp(score - lse)."""
+    B, S, D, Hq, Hkv = 1, 24, 3, 2, 1
+    dh = S  # value row j = e_j, so out[i, j] is the weight of key j
+    for r in range(D):
+        q = _rand((B, S // D, Hq, dh), 20 + r)
+        k = _rand((B, S, Hkv, dh), 30)
+        v = np.eye(S).reshape(1, S, 1, S)
+        out, lse = o.causal_attention(q, k, v, D, r)
+        pos = np.arange(r * (S // (2 * D)), (r + 1) * (S // (2 * D)))
+        pos = np.concatenate([pos, np.arange((2 * D - 1 - r) * (S // (2 * D)), (2 * D - r) * (S // (2 * D)))])
+        for h in range(Hq):
+            P = out[0, :, h, :]
+            assert np.allclose(P.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+            for i, p in enumerate(pos):
+                assert np.all(P[i, p + 1:] == 0.0), (r, h, i)
+                assert np.all(P[i, :p + 1] > 0.0), (r, h, i)
+                s = (q[0, i, h] @ k[0, :p + 1, 0].T) / math.sqrt(dh)
+                assert np.allclose(P[i, :p + 1], np.exp(s - lse[0, h, i]), rtol=1e-12, atol=0)
+
+
+def pin_values_ones(o):
+    """v = 1 everywhere gives out = 1 (weights are normalised)."""
+    q, k, _ = _tiny_inputs((1, 32, 4, 2, 4, 2, 8), 40)
+    out, _ = o.causal_attention(q, k, np.ones_like(k), 4, 2)
+    assert np.allclose(out, 1.0, rtol=0, atol=1e-13)
+
+
+def pin_zero_queries(o):
+    """q = 0: every visible key weighs the same, so out is the prefix mean of v and
+    lse = ln(position + 1)."""
+    B, S, D, Hq, Hkv, dh = 1, 64, 4, 4, 2, 8
+    k = _rand((B, S, Hkv, dh), 50)
+    v = _rand((B, S, Hkv, dh), 51)
+    for r in range(D):
+        q = np.zeros((B, S // D, Hq, dh))
+        out, lse = o.causal_attention(q, k, v, D, r)
+        C = S // (2 * D)
+        pos = np.concatenate([np.arange(r * C, (r + 1) * C), np.arange((2 * D - 1 - r) * C, (2 * D - r) * C)])
+        for h in range(Hq):
+            hk = h // (Hq // Hkv)
+            prefix_mean = np.cumsum(v[0, :, hk, :], axis=0) / np.arange(1, S + 1)[:, None]
+            assert np.allclose(out[0, :, h, :], prefix_mean[pos], rtol=0, atol=1e-13), (r, h)
+            assert np.allclose(lse[0, h, :], np.log(pos + 1.0), rtol=0, atol=1e-13), (r, h)
+
+
+def pin_first_position(o):
+    """The query at global position 0 sees only key 0: out = v_0, lse = q.k_0 / sqrt(dh)."""
+    for dh in (4, 16, 64):
+        q, k, v = _tiny_inputs((1, 32, 4, 0, 2, 1, dh), 60 + dh)
+        out, lse = o.causal_attention(q, k, v, 4, 0)
+        for h in range(2):
+            assert np.allclose(out[0, 0, h], v[0, 0, 0], rtol=0, atol=1e-14)
+            assert abs(lse[0, h, 0] - q[0, 0, h] @ k[0, 0, 0] / math.sqrt(dh)) < 1e-13
+
+
+def pin_gqa_equivalence(o):
+    """Grouped-query attention == multi-head attention on repeated K/V heads."""
+    B, S, D, r, Hq, Hkv, dh = 1, 48, 3, 1, 6, 2, 8
+    q, k, v = _tiny_inputs((B, S, D, r, Hq, Hkv, dh), 70)
+    out_g, lse_g = o.causal_attention(q, k, v, D, r)
+    grp = Hq // Hkv
+    out_m, lse_m = o.causal_attention(q, np.repeat(k, grp, axis=2), np.repeat(v, grp, axis=2), D, r)
+    assert np.allclose(out_g, out_m, rtol=0, atol=1e-13)
+    assert np.allclose(lse_g, lse_m, rtol=0, atol=1e-13)
+
+
+def pin_shift_invariance(o):
+    """Adding c to every key leaves out unchanged and shifts lse by q.c / sqrt(dh)."""
+    B, S, D, r, Hq, Hkv, dh = 1, 32, 2, 1, 2, 1, 8
+    q, k, v = _tiny_inputs((B, S, D, r, Hq, Hkv, dh), 80)
+    c = _rand((dh,), 81)
+    out0, lse0 = o.causal_attention(q, k, v, D, r)
+    out1, lse1 = o.causal_attention(q, k + c, v, D, r)
+    assert np.allclose(out0, out1, rtol=0, atol=1e-12)
+    shift = np.einsum("bshd,d->bhs", q, c) / math.sqrt(dh)
+    assert np.allclose(lse1 - lse0, shift, rtol=0, atol=1e-12)
+
+
+ALL_PINS = [
+    pin_zigzag_golden,
+    pin_zigzag_permutation,
+    pin_pairs_closed_form,
+    pin_gqa_ownership,
+    pin_bruteforce,
+    pin_sdpa_one_rank,
+    pin_concatenation,
+    pin_probabilities,
+    pin_values_ones,
+    pin_zero_queries,
+    pin_first_position,
+    pin_gqa_equivalence,
+    pin_shift_invariance,
+]

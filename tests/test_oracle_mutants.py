@@ -1,0 +1,125 @@
+"""Planted mistakes in the oracle must each trip at least one pin (CPU only).
+
+Every mutant is a copy of the oracle with one plausible error: a swapped or mirrored
+chunk, a strict causal diagonal, interleaved GQA grouping, a wrong softmax scale, a
+base-2 lse, a dropped normalisation, swapped K/V operands, local instead of global
+positions, or a block-boundary error in the blocked form.
+"""
+
+import types
+
+import numpy as np
+import pytest
+
+import oracle.attention as A
+from pins import ALL_PINS
+
+
+def _zz_swapped(S, D, r):
+    pos = A_orig_zigzag(S, D, r)
+    C = S // (2 * D)
+    return np.concatenate([pos[C:], pos[:C]])
+
+
+def _zz_mirror_off_by_one(S, D, r):
+    C = S // (2 * D)
+    hi = (2 * D - r) % (2 * D)
+    return np.concatenate([np.arange(r * C, (r + 1) * C), np.arange(hi * C, (hi + 1) * C)])
+
+
+def _zz_local(S, D, r):
+    return np.arange(S // D, dtype=np.int64)
+
+
+A_orig_zigzag = A.zigzag_positions
+
+PATCHES = {
+    "chunk_order_swapped": ("zigzag_positions", _zz_swapped),
+    "mirror_chunk_off_by_one": ("zigzag_positions", _zz_mirror_off_by_one),
+    "local_positions": ("zigzag_positions", _zz_local),
+    "strict_diagonal": ("visible", lambda j, p: j[None, :] < p[:, None]),
+    "gqa_interleaved": ("kv_head_of", lambda h, Hq, Hkv: h % Hkv),
+    "scale_one_over_dh": ("softmax_scale", lambda dh: 1.0 / dh),
+    "no_scale": ("softmax_scale", lambda dh: 1.0),
+}
+
+
+def _lse_log2(f):
+    def g(*a, **kw):
+        out, lse = f(*a, **kw)
+        return out, lse / np.log(2.0)
+    return g
+
+
+def _unnormalised(f):
+    def g(*a, **kw):
+        out, lse = f(*a, **kw)
+        return out * np.exp(lse).transpose(0, 2, 1)[..., None], lse
+    return g
+
+
+def _kv_swapped(f):
+    def g(q, k, v, *a, **kw):
+        return f(q, v, k, *a, **kw)
+    return g
+
+
+def _block_drops_last_row(f):
+    def g(q, k, v, D, rank, rows=None, heads=None, block=256):
+        out, lse = f(q, k, v, D, rank, rows=rows, heads=heads, block=block)
+        out = out.copy()
+        out[:, block - 1::block] = 0.0  # last row of every block lost
+        return out, lse
+    g.__wrapped_blocked__ = True
+    return g
+
+
+WRAPS = {
+    "lse_base2": _lse_log2,
+    "dropped_normalisation": _unnormalised,
+    "kv_swapped": _kv_swapped,
+}
+
+
+def _namespace():
+    ns = types.SimpleNamespace()
+    for n in ("causal_attention", "causal_attention_bruteforce", "zigzag_positions",
+              "unmasked_pairs", "kv_head_of"):
+        setattr(ns, n, getattr(A, n))
+    return ns
+
+
+def _failures(ns):
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(ns)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(PATCHES))
+def test_patched_mutant_is_caught(name, monkeypatch):
+    attr, fn = PATCHES[name]
+    monkeypatch.setattr(A, attr, fn)
+    with np.errstate(all="ignore"):
+        failed = _failures(_namespace())
+    assert failed, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(WRAPS))
+def test_wrapped_mutant_is_caught(name):
+    ns = _namespace()
+    ns.causal_attention = WRAPS[name](A.causal_attention)
+    ns.causal_attention_bruteforce = WRAPS[name](A.causal_attention_bruteforce)
+    with np.errstate(all="ignore"):
+        failed = _failures(ns)
+    assert failed, f"mutant {name} passed every pin"
+
+
+def test_blocked_form_error_is_caught():
+    ns = _namespace()
+    ns.causal_attention = _block_drops_last_row(A.causal_attention)
+    failed = _failures(ns)
+    assert "pin_bruteforce" in failed
