@@ -1,0 +1,188 @@
+"""Benchmark: causal attention forward of one sequence-parallel rank on one MI355X.
+
+One step = one call of the whole hot path (zigzag map, K/V tile staging, QK^T, causal
+masking and tile skipping, online softmax, PV, epilogue: one kernel launch) over the
+7B-dense TSP shard: B=1, S_total=32768, D=8, rank 3 (chunks 3 and 12, 4096 local
+queries), Hq=Hkv=32, dh=128, bf16, synthetic N(0,1) inputs already resident in HBM.
+
+Prints ONE JSON line. `value` is causal TFLOP/s = 4*B*Hq*dh*C*(S_total+1) / time per
+step (visible (q,k) pairs only; softmax not counted). The roofline entry compares the
+kernel's algorithmic FLOP rate, timed with HIP events on its own stream, with the
+MI355X dense bf16 MFMA peak. The cpu_baseline entry times the fp64 CPU oracle on a
+bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz (AMD's 2.5 PFLOP/s)
+PEAK_F32_MFMA_TFLOPS = 157.3
+METRIC = "causal attention TFLOP/s per rank shard + % of bf16 MFMA peak (1 GPU)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_digest() -> str:
+    csrc = os.path.join(ROOT, "sequence_causal_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str, flops_per_launch: float):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken
+    on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload_name)
+    if not entry or entry.get("source_digest") != kernel_source_digest():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, rank, q, k, v, budget_s: float):
+    """The fp64 oracle on a bounded sample: leading rows of each chunk, a few heads."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: fall back to the affinity mask
+        threads = len(os.sched_getaffinity(0))
+    pos = oracle.zigzag_positions(w.S_total, w.D, rank)
+    heads, n_rows = [0, 1], 128
+    rows = np.concatenate([np.arange(0, n_rows), np.arange(w.C, w.C + n_rows)])
+    pairs = int(np.sum(pos[rows] + 1))
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        oracle.causal_attention(q, k, v, w.D, rank, rows=rows, heads=heads, block=128)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s or done >= 64:
+            break
+    dt = (time.perf_counter() - t0) / done
+    flops = 4.0 * w.B * len(heads) * w.dh * pairs
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(min(threads, len(os.sched_getaffinity(0)))),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, rank {rank} rows [0,{n_rows}) and [{w.C},{w.C + n_rows}) "
+                   f"(both chunks), query heads {heads}, all visible keys; {done} pass(es), "
+                   f"{dt:.2f} s each; same algorithmic FLOP count convention"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="tsp_7b_shard_s32k")
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the per-rank attention on a single "
+              "MI355X and has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sequence_causal_attention_amd as tsp
+    import workloads
+
+    w = workloads.BY_NAME[args.workload]
+    rank = w.ranks[0] if args.rank is None else args.rank
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    q, k, v = workloads.make_inputs(w, rank)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.S_local), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(dev)  # default priority
+    torch.cuda.synchronize()
+
+    def step():
+        tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    flops = 4.0 * w.B * w.Hq * w.dh * w.C * (w.S_total + 1)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, rank, q, k, v, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "S_total": w.S_total, "D": w.D, "rank": rank, "Hq": w.Hq,
+            "Hkv": w.Hkv, "dh": w.dh, "local_queries": w.S_local, "flops_per_step": flops,
+            "parallelism": "one sequence-parallel rank's shard on 1 GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(w.name, flops),
+            "kernel_ms": round(kernel_ms, 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

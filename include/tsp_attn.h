@@ -1,0 +1,128 @@
+/*
+ * tsp_attn.h -- C ABI of the per-rank zigzag / GQA causal attention forward for MI355X
+ * (gfx950).
+ *
+ * The operation: one sequence-parallel rank holds a zigzag share of the queries and
+ * attends causally to the all-gathered full-sequence keys and values
+ * ("Folding Tensor and Sequence Parallelism for Memory-Efficient Transformer Training &
+ * Inference", section 2 Methodology, attention layers: all-gather of K/V along the
+ * sequence, attention of the local queries, zigzag partitioning for causal balance).
+ * Causal visibility is decided by global token position, recomputed for the sharded
+ * layout ("AutoSP: Unlocking Long-Context LLM Training Via Compiler-Based Sequence
+ * Parallelism", section 2.A, item 4). Query heads are grouped over KV heads
+ * ("Tensor, pipeline e sequence parallelism", section 01, GQA paragraph); D = 1 is the
+ * Ulysses case of full attention over a head subset (same page, sequence-parallel
+ * paragraph).
+ *
+ * Conventions shared by every entry point:
+ *  - Zigzag map: the sequence of S_total tokens is cut into 2*D chunks of
+ *    C = S_total / (2*D); rank r holds chunk r in local rows [0, C) and chunk 2*D-1-r in
+ *    local rows [C, 2C). Local row i has global position
+ *        g(i) = r*C + i                 for i <  C
+ *        g(i) = (2*D-1-r)*C + (i - C)   for i >= C.
+ *    With D = 1 the map is the identity.
+ *  - Key j is visible to local row i iff j <= g(i) (inclusive diagonal).
+ *  - Query head h reads KV head h / (Hq / Hkv) (contiguous grouping).
+ *  - Scores are scaled by 1/sqrt(dh); lse is the natural-log log-sum-exp of the scaled
+ *    scores over the visible keys.
+ *
+ * Status codes: every int-returning function returns TSP_OK (0) or a negative code.
+ * Arguments are validated before anything is enqueued, so on error nothing is launched
+ * and no output byte is written. No C++ exception crosses this boundary. A message for
+ * the calling thread's last failure is available from tsp_attn_last_error().
+ *
+ * Ownership: all buffers belong to the caller. The library allocates no device memory,
+ * frees nothing and keeps no pointer after a call returns. Work is enqueued
+ * asynchronously on the caller's stream on the current HIP device; the library never
+ * synchronizes the stream.
+ */
+#ifndef TSP_ATTN_H
+#define TSP_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TSP_OK 0
+#define TSP_EINVAL (-1)       /* bad pointer, size, rank or divisibility */
+#define TSP_EUNSUPPORTED (-2) /* head dim or element type without a kernel */
+#define TSP_ELAUNCH (-3)      /* the HIP runtime rejected the launch */
+#define TSP_EINTERNAL (-4)    /* a HIP runtime query failed */
+
+/* element types of q_local / k_full / v_full / out */
+#define TSP_BF16 0 /* bfloat16, MFMA bf16 products, fp32 accumulation */
+#define TSP_F32 1  /* float32, MFMA fp32 products, fp32 accumulation */
+
+/*
+ * tsp_attn_fwd -- causal attention of one rank's zigzag queries against the full K/V.
+ *
+ *   q_local  device, [B, 2C, Hq, dh] contiguous (BSHD), element type `dtype`
+ *   k_full   device, [B, S_total, Hkv, dh] contiguous, row j = global token j
+ *   v_full   device, [B, S_total, Hkv, dh] contiguous, row j = global token j
+ *   out      device, [B, 2C, Hq, dh] contiguous, element type `dtype` (written)
+ *   lse      device, [B, Hq, 2C] float32 (written)
+ *   B, S_total, D, rank, Hq, Hkv, dh   sizes as above; C = S_total / (2*D)
+ *   dtype    TSP_BF16 or TSP_F32
+ *   stream   a hipStream_t (NULL = the default stream)
+ *
+ * Requirements: B >= 1, D >= 1, 0 <= rank < D, S_total > 0 and divisible by 2*D,
+ * Hq >= 1, Hkv >= 1, Hq divisible by Hkv, dh in {64, 128, 256}, all pointers non-NULL
+ * and 16-byte aligned, out/lse not overlapping the inputs. Keys past the largest global
+ * position of the rank's queries are never read, so they may hold anything.
+ * Rounding: out is the fp32 result rounded to nearest-even in `dtype`.
+ * Returns TSP_OK, TSP_EINVAL, TSP_EUNSUPPORTED or TSP_ELAUNCH.
+ */
+int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, void* out,
+                 float* lse, int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq,
+                 int64_t Hkv, int64_t dh, int dtype, void* stream);
+
+/*
+ * tsp_attn_zigzag_positions -- the zigzag map on the host: writes g(i) for the 2C local
+ * rows of `rank` into out_host (caller-owned host memory of 2C int64).
+ * ("Folding Tensor and Sequence Parallelism ...", section 2, zigzag partitioning.)
+ * Returns TSP_OK or TSP_EINVAL.
+ */
+int tsp_attn_zigzag_positions(int64_t S_total, int64_t D, int64_t rank, int64_t* out_host);
+
+/*
+ * tsp_attn_zigzag_positions_device -- the same map as evaluated by the attention
+ * kernel's own device code: writes g(i) for the 2C local rows into out_dev
+ * (caller-owned device memory of 2C int32), enqueued on `stream`. Positions are below
+ * 2^31 by the S_total limit checked here. Returns TSP_OK, TSP_EINVAL or TSP_ELAUNCH.
+ */
+int tsp_attn_zigzag_positions_device(int32_t* out_dev, int64_t S_total, int64_t D,
+                                     int64_t rank, void* stream);
+
+/*
+ * tsp_attn_unmasked_pairs -- visible (query, key) pairs of `rank` per (batch, query head):
+ * the sum over local rows of g(i) + 1. Equal for every rank: C * (S_total + 1).
+ * Returns the count, or TSP_EINVAL for invalid arguments.
+ */
+int64_t tsp_attn_unmasked_pairs(int64_t S_total, int64_t D, int64_t rank);
+
+/*
+ * tsp_attn_schedule -- the work decomposition tsp_attn_fwd launches for these sizes:
+ * writes the number of workgroups to *n_workgroups and, if kv_tiles_per_workgroup is
+ * non-NULL, the number of key/value tiles each workgroup processes (caller-owned host
+ * memory of at least *n_workgroups int64; call once with NULL to size it), and the key
+ * tile length to *kv_tile (may be NULL). Pure host computation.
+ * Returns TSP_OK, TSP_EINVAL or TSP_EUNSUPPORTED.
+ */
+int tsp_attn_schedule(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq,
+                      int64_t Hkv, int64_t dh, int dtype, int64_t* n_workgroups,
+                      int64_t* kv_tiles_per_workgroup, int64_t* kv_tile);
+
+/* tsp_attn_strerror -- static description of a status code. */
+const char* tsp_attn_strerror(int status);
+
+/* tsp_attn_last_error -- message of the calling thread's last failed call ("" if none). */
+const char* tsp_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSP_ATTN_H */

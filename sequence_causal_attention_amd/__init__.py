@@ -1,0 +1,177 @@
+"""Python binding of the MI355X per-rank zigzag / GQA causal attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libtsp_attn.so`` (built from ``csrc/`` by ``python -m sequence_causal_attention_amd.build``).
+PyTorch provides device memory and the stream. There is no fallback: if the library is
+missing or a call fails, an exception is raised.
+
+The operation ("Folding Tensor and Sequence Parallelism for Memory-Efficient Transformer
+Training & Inference", section 2, attention layers; "AutoSP ...", section 2.A item 4;
+"Tensor, pipeline e sequence parallelism", section 01, GQA and sequence-parallel
+paragraphs): rank ``rank`` of ``D`` holds chunks ``rank`` and ``2D-1-rank`` of the
+sequence (2D chunks of C = S_total/(2D) tokens) as its local queries and attends
+causally, by global position, to the full-sequence keys/values.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtsp_attn.so")
+
+TSP_OK = 0
+TSP_EINVAL = -1
+TSP_EUNSUPPORTED = -2
+TSP_ELAUNCH = -3
+TSP_EINTERNAL = -4
+TSP_BF16 = 0
+TSP_F32 = 1
+
+# Every entry point the header declares, with its ctypes signature.
+_I64 = ctypes.c_int64
+_VP = ctypes.c_void_p
+SIGNATURES = {
+    "tsp_attn_fwd": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                    ctypes.c_int, _VP]),
+    "tsp_attn_zigzag_positions": (ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(_I64)]),
+    "tsp_attn_zigzag_positions_device": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP]),
+    "tsp_attn_unmasked_pairs": (_I64, [_I64, _I64, _I64]),
+    "tsp_attn_schedule": (ctypes.c_int, [_I64, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_int,
+                                         ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "tsp_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "tsp_attn_last_error": (ctypes.c_char_p, []),
+}
+
+_lib_handle = None
+
+
+class TspAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"tsp_attn status {status}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m sequence_causal_attention_amd.build`"
+            )
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def _check(status: int):
+    if status != TSP_OK:
+        msg = lib().tsp_attn_last_error().decode() or lib().tsp_attn_strerror(status).decode()
+        raise TspAttnError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TSP_BF16
+    if t.dtype == torch.float32:
+        return TSP_F32
+    raise TspAttnError(TSP_EUNSUPPORTED, f"unsupported element type {t.dtype}")
+
+
+def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D: int, rank: int,
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+    """Causal attention of this rank's zigzag queries against the full K/V.
+
+    q_local [B, 2C, Hq, dh], k_full / v_full [B, S_total, Hkv, dh]: contiguous, same
+    device and dtype (bf16 or fp32). Returns (out [B, 2C, Hq, dh] same dtype,
+    lse [B, Hq, 2C] fp32). ``out`` / ``lse`` may be passed in preallocated.
+    The call is asynchronous on ``stream`` (default: the current stream).
+    """
+    for name, t in (("q_local", q_local), ("k_full", k_full), ("v_full", v_full)):
+        if not t.is_cuda:
+            raise TspAttnError(TSP_EINVAL, f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise TspAttnError(TSP_EINVAL, f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise TspAttnError(TSP_EINVAL, f"{name} must be 4-D [B, S, H, dh]")
+    if not (q_local.dtype == k_full.dtype == v_full.dtype):
+        raise TspAttnError(TSP_EINVAL, "q_local, k_full and v_full must share one dtype")
+    if not (q_local.device == k_full.device == v_full.device):
+        raise TspAttnError(TSP_EINVAL, "inputs must be on one device")
+    B, S_local, Hq, dh = q_local.shape
+    Bk, S_total, Hkv, dhk = k_full.shape
+    if tuple(v_full.shape) != tuple(k_full.shape) or Bk != B or dhk != dh:
+        raise TspAttnError(TSP_EINVAL, "k_full / v_full must be [B, S_total, Hkv, dh] matching q_local")
+    if D < 1 or S_total % (2 * D) != 0 or S_local != S_total // D:
+        raise TspAttnError(TSP_EINVAL, f"q_local must hold S_total / D = {S_total // max(D, 1)} rows")
+    code = _dtype_code(q_local)
+    if out is None:
+        out = torch.empty_like(q_local)
+    if lse is None:
+        lse = torch.empty((B, Hq, S_local), dtype=torch.float32, device=q_local.device)
+    if out.shape != q_local.shape or out.dtype != q_local.dtype or not out.is_contiguous():
+        raise TspAttnError(TSP_EINVAL, "out must match q_local")
+    if tuple(lse.shape) != (B, Hq, S_local) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TspAttnError(TSP_EINVAL, "lse must be float32 [B, Hq, S_local]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q_local.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q_local.device):
+        st = lib().tsp_attn_fwd(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, code, handle)
+    _check(st)
+    return out, lse
+
+
+def fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, S_total, D, rank, Hq, Hkv, dh, dtype, stream) -> int:
+    """Direct call of the C entry point with raw pointers; returns the status code."""
+    return lib().tsp_attn_fwd(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, S_total, D, rank, Hq, Hkv, dh, dtype,
+                              stream)
+
+
+def zigzag_positions(S_total: int, D: int, rank: int) -> torch.Tensor:
+    """Host-side zigzag map of the library: global position of each local row (int64)."""
+    if D < 1 or S_total % (2 * D) != 0:
+        _check(lib().tsp_attn_zigzag_positions(S_total, D, rank, None))
+    n = S_total // D
+    out = torch.empty(n, dtype=torch.int64)
+    _check(lib().tsp_attn_zigzag_positions(S_total, D, rank,
+                                           ctypes.cast(out.data_ptr(), ctypes.POINTER(_I64))))
+    return out
+
+
+def zigzag_positions_device(S_total: int, D: int, rank: int, device="cuda") -> torch.Tensor:
+    """The zigzag map as evaluated by the kernels' device code (int32, on ``device``)."""
+    n = S_total // D if D >= 1 else 0
+    out = torch.empty(max(n, 1), dtype=torch.int32, device=device)
+    with torch.cuda.device(out.device):
+        st = lib().tsp_attn_zigzag_positions_device(out.data_ptr(), S_total, D, rank,
+                                                    torch.cuda.current_stream(out.device).cuda_stream)
+    _check(st)
+    return out[:n]
+
+
+def unmasked_pairs(S_total: int, D: int, rank: int) -> int:
+    r = lib().tsp_attn_unmasked_pairs(S_total, D, rank)
+    if r < 0:
+        _check(int(r))
+    return int(r)
+
+
+def schedule(B, S_total, D, rank, Hq, Hkv, dh, dtype=TSP_BF16):
+    """(n_workgroups, kv tiles per workgroup [int64 tensor], kv tile length) of a launch."""
+    n = _I64(0)
+    _check(lib().tsp_attn_schedule(B, S_total, D, rank, Hq, Hkv, dh, dtype, ctypes.byref(n), None, None))
+    tiles = torch.empty(n.value, dtype=torch.int64)
+    bk = _I64(0)
+    _check(lib().tsp_attn_schedule(B, S_total, D, rank, Hq, Hkv, dh, dtype, ctypes.byref(n),
+                                   ctypes.cast(tiles.data_ptr(), ctypes.POINTER(_I64)), ctypes.byref(bk)))
+    return n.value, tiles, bk.value

@@ -1,0 +1,231 @@
+// tsp_attn.hip -- C ABI of the per-rank zigzag / GQA causal attention forward (gfx950):
+// argument validation, work decomposition, kernel dispatch, the zigzag map helpers and
+// the error strings. The operation and every argument are documented in tsp_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+
+#include "tsp_attn.h"
+#include "attn_common.h"
+#include "attn_fwd_bf16.h"
+#include "attn_fwd_f32.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  if (std::getenv("TSP_ATTN_DEBUG")) std::fprintf(stderr, "tsp_attn: %s\n", g_last_error);
+  return status;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Tile configuration of one (dtype, dh) kernel.
+struct KernelShape {
+  int kv_tile;     // keys per K/V tile
+  int waves;       // waves per workgroup
+  int row_blocks;  // 32-row query blocks per wave
+};
+
+bool kernel_shape(int dtype, int64_t dh, KernelShape* ks) {
+  if (dh != 64 && dh != 128 && dh != 256) return false;
+  if (dtype == TSP_BF16) {
+    *ks = KernelShape{dh == 256 ? 32 : 64, 4, 1};
+    return true;
+  }
+  if (dtype == TSP_F32) {
+    *ks = KernelShape{32, 4, 1};
+    return true;
+  }
+  return false;
+}
+
+int check_sizes(int64_t S_total, int64_t D, int64_t rank) {
+  if (D < 1) return fail(TSP_EINVAL, "D must be >= 1 (got %lld)", (long long)D);
+  if (rank < 0 || rank >= D) return fail(TSP_EINVAL, "rank %lld outside [0, %lld)", (long long)rank, (long long)D);
+  if (S_total <= 0) return fail(TSP_EINVAL, "S_total must be > 0 (got %lld)", (long long)S_total);
+  if (S_total % (2 * D) != 0)
+    return fail(TSP_EINVAL, "S_total %lld not divisible by 2*D = %lld", (long long)S_total, (long long)(2 * D));
+  if (S_total > (int64_t(1) << 30)) return fail(TSP_EINVAL, "S_total %lld above 2^30", (long long)S_total);
+  return TSP_OK;
+}
+
+// Validates everything but pointers and builds the launch parameters.
+int plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
+         TspParams* p, KernelShape* ks) {
+  int st = check_sizes(S_total, D, rank);
+  if (st != TSP_OK) return st;
+  if (B < 1) return fail(TSP_EINVAL, "B must be >= 1 (got %lld)", (long long)B);
+  if (Hq < 1 || Hkv < 1) return fail(TSP_EINVAL, "Hq and Hkv must be >= 1");
+  if (Hq % Hkv != 0) return fail(TSP_EINVAL, "Hq %lld not divisible by Hkv %lld", (long long)Hq, (long long)Hkv);
+  if (dtype != TSP_BF16 && dtype != TSP_F32) return fail(TSP_EUNSUPPORTED, "unknown dtype %d", dtype);
+  if (!kernel_shape(dtype, dh, ks)) return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
+  if (Hq > 65536 || B > 65536) return fail(TSP_EINVAL, "B or Hq too large");
+
+  const int64_t C = S_total / (2 * D);
+  const int64_t grp = Hq / Hkv;
+  const int rows_per_wg = 32 * ks->waves * ks->row_blocks;
+  // Query heads per workgroup: the largest divisor of grp that also divides the
+  // workgroup's row blocks, so one K/V tile in LDS serves as many heads as possible.
+  int64_t GH = 1;
+  for (int64_t g = 1; g <= grp; ++g)
+    if (grp % g == 0 && (ks->waves * ks->row_blocks) % g == 0) GH = g;
+  const int64_t BQ = rows_per_wg / GH;
+  const int64_t n_qtiles = (2 * C + BQ - 1) / BQ;
+  const int64_t n_pairs = (n_qtiles + 1) / 2;
+  const int64_t n_units = B * Hkv * (grp / GH) * n_pairs;
+  if (n_units > 0x7fffffff) return fail(TSP_EINVAL, "problem too large for one launch");
+
+  p->S_total = (int32_t)S_total;
+  p->C = (int32_t)C;
+  p->S_local = (int32_t)(2 * C);
+  p->D = (int32_t)D;
+  p->rank = (int32_t)rank;
+  p->Hq = (int32_t)Hq;
+  p->Hkv = (int32_t)Hkv;
+  p->grp = (int32_t)grp;
+  p->GH = (int32_t)GH;
+  p->BQ = (int32_t)BQ;
+  p->n_qtiles = (int32_t)n_qtiles;
+  p->n_pairs = (int32_t)n_pairs;
+  p->n_hgroups = (int32_t)(grp / GH);
+  p->n_units = (int32_t)n_units;
+  p->scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  return TSP_OK;
+}
+
+template <int DH, int BK, int NW, int RB>
+void launch_bf16(const TspParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, BK, NW, RB>), dim3(p.n_units), dim3(NW * 64), 0, stream, p);
+}
+
+template <int DH>
+void launch_f32(const TspParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((tsp::attn_fwd_f32_kernel<DH>), dim3(p.n_units), dim3(256), 0, stream, p);
+}
+
+__global__ void zigzag_dump_kernel(int32_t* out, int32_t n, int32_t C, int32_t D, int32_t rank) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = tsp_zigzag_position(i, C, D, rank);
+}
+
+}  // namespace
+
+extern "C" {
+
+int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse, int64_t B,
+                 int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
+                 void* stream) {
+  if (!q_local || !k_full || !v_full || !out || !lse) return fail(TSP_EINVAL, "null pointer argument");
+  if (!aligned16(q_local) || !aligned16(k_full) || !aligned16(v_full) || !aligned16(out) || !aligned16(lse))
+    return fail(TSP_EINVAL, "pointers must be 16-byte aligned");
+  TspParams p{};
+  KernelShape ks{};
+  int st = plan(B, S_total, D, rank, Hq, Hkv, dh, dtype, &p, &ks);
+  if (st != TSP_OK) return st;
+  p.q = q_local;
+  p.k = k_full;
+  p.v = v_full;
+  p.out = out;
+  p.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so the check below reports this launch
+  if (dtype == TSP_BF16) {
+    switch (dh) {
+      case 64: launch_bf16<64, 64, 4, 1>(p, s); break;
+      case 128: launch_bf16<128, 64, 4, 1>(p, s); break;
+      case 256: launch_bf16<256, 32, 4, 1>(p, s); break;
+    }
+  } else {
+    switch (dh) {
+      case 64: launch_f32<64>(p, s); break;
+      case 128: launch_f32<128>(p, s); break;
+      case 256: launch_f32<256>(p, s); break;
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TSP_ELAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return TSP_OK;
+}
+
+int tsp_attn_zigzag_positions(int64_t S_total, int64_t D, int64_t rank, int64_t* out_host) {
+  int st = check_sizes(S_total, D, rank);
+  if (st != TSP_OK) return st;
+  if (!out_host) return fail(TSP_EINVAL, "null output pointer");
+  const int32_t C = (int32_t)(S_total / (2 * D));
+  for (int32_t i = 0; i < 2 * C; ++i) out_host[i] = tsp_zigzag_position(i, C, (int32_t)D, (int32_t)rank);
+  return TSP_OK;
+}
+
+int tsp_attn_zigzag_positions_device(int32_t* out_dev, int64_t S_total, int64_t D, int64_t rank, void* stream) {
+  int st = check_sizes(S_total, D, rank);
+  if (st != TSP_OK) return st;
+  if (!out_dev) return fail(TSP_EINVAL, "null output pointer");
+  const int32_t C = (int32_t)(S_total / (2 * D));
+  const int32_t n = 2 * C;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(zigzag_dump_kernel, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     out_dev, n, C, (int32_t)D, (int32_t)rank);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TSP_ELAUNCH, "map kernel launch failed: %s", hipGetErrorString(e));
+  return TSP_OK;
+}
+
+int64_t tsp_attn_unmasked_pairs(int64_t S_total, int64_t D, int64_t rank) {
+  int st = check_sizes(S_total, D, rank);
+  if (st != TSP_OK) return st;
+  const int32_t C = (int32_t)(S_total / (2 * D));
+  int64_t total = 0;
+  for (int32_t i = 0; i < 2 * C; ++i) total += (int64_t)tsp_zigzag_position(i, C, (int32_t)D, (int32_t)rank) + 1;
+  return total;
+}
+
+int tsp_attn_schedule(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh,
+                      int dtype, int64_t* n_workgroups, int64_t* kv_tiles_per_workgroup, int64_t* kv_tile) {
+  if (!n_workgroups) return fail(TSP_EINVAL, "null n_workgroups");
+  TspParams p{};
+  KernelShape ks{};
+  int st = plan(B, S_total, D, rank, Hq, Hkv, dh, dtype, &p, &ks);
+  if (st != TSP_OK) return st;
+  *n_workgroups = p.n_units;
+  if (kv_tile) *kv_tile = ks.kv_tile;
+  if (kv_tiles_per_workgroup) {
+    for (int64_t u = 0; u < p.n_units; ++u) {
+      const int32_t pair = (int32_t)(u % p.n_pairs);
+      int64_t tiles = 0;
+      for (int which = 0; which < 2; ++which) {
+        const int32_t qt = which == 0 ? p.n_qtiles - 1 - pair : pair;
+        if (which == 1 && qt == p.n_qtiles - 1 - pair) break;
+        const int32_t last_row = std::min(qt * p.BQ + p.BQ, p.S_local) - 1;
+        const int64_t kv_end = (int64_t)tsp_zigzag_position(last_row, p.C, p.D, p.rank) + 1;
+        tiles += (kv_end + ks.kv_tile - 1) / ks.kv_tile;
+      }
+      kv_tiles_per_workgroup[u] = tiles;
+    }
+  }
+  return TSP_OK;
+}
+
+const char* tsp_attn_strerror(int status) {
+  switch (status) {
+    case TSP_OK: return "success";
+    case TSP_EINVAL: return "invalid argument";
+    case TSP_EUNSUPPORTED: return "unsupported head dimension or element type";
+    case TSP_ELAUNCH: return "kernel launch failed";
+    case TSP_EINTERNAL: return "internal HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* tsp_attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, its host-side
+zigzag map and pair count agree bit-exactly with the oracle, its schedule is balanced,
+and invalid arguments are rejected before anything is launched (no GPU needed: every
+call here returns during host-side validation or is a pure host computation)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import sequence_causal_attention_amd as tsp
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsp_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsp_attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tsp.LIB_PATH):
+        pytest.fail(f"{tsp.LIB_PATH} not built: run `python -m sequence_causal_attention_amd.build`")
+    return tsp.lib()
+
+
+def test_header_declares_the_binding_surface():
+    assert declared_functions() == sorted(tsp.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", tsp.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {ln.split()[-1] for ln in out.stdout.splitlines() if ln.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_library_links_no_torch():
+    out = subprocess.run(["ldd", tsp.LIB_PATH], capture_output=True, text=True)
+    assert "torch" not in out.stdout and "c10" not in out.stdout
+
+
+MAP_CASES = [(2, 1, 0), (8, 4, 3), (512, 4, 1), (1200, 3, 2), (32768, 8, 3), (262144, 8, 0), (262144, 8, 7),
+             (131072, 1, 0), (65536, 4, 2)]
+
+
+@pytest.mark.parametrize("S,D,r", MAP_CASES)
+def test_host_map_matches_oracle_bit_exact(lib, S, D, r):
+    got = tsp.zigzag_positions(S, D, r).numpy()
+    assert got.dtype == np.int64
+    assert np.array_equal(got, oracle.zigzag_positions(S, D, r))
+
+
+@pytest.mark.parametrize("S,D,r", MAP_CASES)
+def test_unmasked_pairs_matches_oracle(lib, S, D, r):
+    assert tsp.unmasked_pairs(S, D, r) == oracle.unmasked_pairs(S, D, r)
+
+
+@pytest.mark.parametrize("w", workloads.WORKLOADS[1:], ids=lambda w: w.name)
+def test_schedule_is_balanced_across_workgroups_and_ranks(lib, w):
+    """Mirrored query-tile pairs: every workgroup sweeps the same number of KV tiles, and
+    every rank launches the same number of workgroups with the same total."""
+    per_rank = []
+    for r in range(w.D):
+        n, tiles, bk = tsp.schedule(w.B, w.S_total, w.D, r, w.Hq, w.Hkv, w.dh)
+        assert n == tiles.numel() > 0
+        assert int(tiles.max()) - int(tiles.min()) <= 1, (r, tiles.min(), tiles.max())
+        per_rank.append((n, int(tiles.sum()), int(tiles.max())))
+    assert len(set(per_rank)) == 1, per_rank
+
+
+def _fake(addr=0x100000):
+    return ctypes.c_void_p(addr)
+
+
+VALID = dict(B=1, S_total=512, D=4, rank=1, Hq=4, Hkv=1, dh=64, dtype=tsp.TSP_F32)
+
+
+def _call(lib, ptrs=None, **kw):
+    a = dict(VALID)
+    a.update(kw)
+    q, k, v, o, l = ptrs if ptrs is not None else (_fake(), _fake(), _fake(), _fake(), _fake())
+    return lib.tsp_attn_fwd(q, k, v, o, l, a["B"], a["S_total"], a["D"], a["rank"], a["Hq"], a["Hkv"], a["dh"],
+                            a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=0), tsp.TSP_EINVAL),
+    (dict(rank=4), tsp.TSP_EINVAL),
+    (dict(rank=-1), tsp.TSP_EINVAL),
+    (dict(S_total=500), tsp.TSP_EINVAL),
+    (dict(S_total=0), tsp.TSP_EINVAL),
+    (dict(B=0), tsp.TSP_EINVAL),
+    (dict(Hq=6, Hkv=4), tsp.TSP_EINVAL),
+    (dict(Hkv=0), tsp.TSP_EINVAL),
+    (dict(dh=96), tsp.TSP_EUNSUPPORTED),
+    (dict(dh=32), tsp.TSP_EUNSUPPORTED),
+    (dict(dtype=7), tsp.TSP_EUNSUPPORTED),
+])
+def test_invalid_arguments_rejected(lib, kw, code):
+    assert _call(lib, **kw) == code
+    assert lib.tsp_attn_last_error().decode() != ""
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    for i in range(5):
+        ptrs = [_fake(), _fake(), _fake(), _fake(), _fake()]
+        ptrs[i] = None
+        assert _call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
+        ptrs[i] = _fake(0x100008)
+        assert _call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
+
+
+def test_map_helpers_reject_bad_sizes(lib):
+    assert lib.tsp_attn_unmasked_pairs(500, 4, 0) == tsp.TSP_EINVAL
+    assert lib.tsp_attn_zigzag_positions(512, 4, 9, None) == tsp.TSP_EINVAL
+    assert lib.tsp_attn_zigzag_positions(512, 4, 0, None) == tsp.TSP_EINVAL  # null output
+    assert lib.tsp_attn_zigzag_positions_device(None, 512, 0, 0, None) == tsp.TSP_EINVAL
+    with pytest.raises(tsp.TspAttnError):
+        tsp.zigzag_positions(500, 4, 0)
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.tsp_attn_strerror(code)
+    assert lib.tsp_attn_strerror(-99) == b"unknown status"
