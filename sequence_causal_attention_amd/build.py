@@ -37,6 +37,8 @@ def command(out: str = LIB, extra=()) -> list:
         "-fPIC",
         "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results in arch VGPRs: the score tiles feed VALU softmax directly
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", os.path.join(ROOT, "include"),
         "-I", CSRC,
         *extra,

@@ -7,66 +7,122 @@
 // softmax over the keys j <= g(i) of the scaled scores q_i . k_j / sqrt(dh), applied to
 // the values of KV head h / grp; plus lse_i, the natural-log log-sum-exp of the scores.
 //
-// Work decomposition (MI355X-specific, not from the pages):
-//  * A workgroup owns one KV head, GH of its query heads, and a pair of query tiles of BQ
-//    local rows: tile n_qtiles-1-p and tile p. Under the zigzag map the two tiles of a
-//    pair need (2D*C + BQ) keys together whatever p and the rank, so every workgroup
-//    does the same work and no rank is slower than another.
-//  * Every wave owns RB row blocks of 32 query rows (32 consecutive local rows of one
-//    head). Scores are computed transposed, S^T = K Q^T (keys along MFMA rows, queries
-//    along MFMA columns), so each lane holds one query column: the row max and row sum
-//    are in-lane except for one exchange between the two 32-lane halves, and the fp32
-//    score accumulator, rounded to bf16, is already the B operand of O^T = V^T P^T.
-//  * K and V tiles of BK keys are staged once per workgroup in LDS and shared by all
-//    waves, hence by all GH query heads of the KV group; the next tile's global loads
-//    are in flight while the current tile is being computed (double buffer, one
-//    barrier per tile). V is transposed while it is written to LDS, its keys placed in
-//    the order the P operand holds them, so every MFMA operand is one 16-byte LDS read.
-//  * KV tiles past the query tile's last global position are never loaded (causal tile
-//    skipping); only tiles that cross a wave's first position are masked element-wise,
-//    by comparing the key index with the query's global position.
-//  * Online softmax in the base-2 domain (log2(e)/sqrt(dh) folded into one FMA) with a
-//    lazily raised running max (see TSP_RESCALE_SLACK).
+// Design for gfx950 (the pages only name "FlashAttention" on other hardware):
+//  * Work unit = one KV head, GH of its query heads, and a mirrored pair of query tiles
+//    of BQ local rows (tile n_qtiles-1-p, then tile p). Under the zigzag map a pair needs
+//    S_total + BQ keys whatever p and the rank, so all workgroups and all ranks do equal
+//    work. Units are laid out so that each XCD gets a contiguous range (same KV head,
+//    sweeping the same K/V tiles through that XCD's L2).
+//  * A wave owns RB row blocks of 32 query rows. Scores are computed transposed,
+//    S^T = K Q^T (keys on MFMA rows, queries on MFMA columns): each lane holds one query
+//    column, so row max / row sum are in-lane plus one swap of the two 32-lane halves,
+//    and the fp32 accumulator, rounded to bf16, is already the B operand of
+//    O^T = V^T P^T. Q^T stays in registers for the whole key sweep.
+//  * K/V are staged in 32-key stages straight from global memory into LDS
+//    (global_load_lds_dwordx4, no register round trip) through a ring of NBUF stages,
+//    PD = NBUF-2 stages ahead of use; every wave issues an equal share of each stage and
+//    waits (vmcnt) only for the stage it needs next. Rows are XOR-swizzled at 16-byte
+//    granularity so both LDS read patterns are bank-conflict free: K as one ds_read_b128
+//    per MFMA operand, V^T through the gfx950 transposing read ds_read_b64_tr_b16 (two
+//    per MFMA operand), which also makes V's key order match the P operand.
+//  * Software pipeline per 32-key step t: the QK^T MFMAs of step t+1 are issued in the
+//    same basic block as the exp2/convert/sum VALU work of step t, and the PV MFMAs of
+//    step t in the same block as the mask/row-max VALU work of step t+1, so matrix and
+//    vector pipes overlap inside one wave.
+//  * Causal tile skipping: the sweep stops at the tile's last global position; keys past
+//    it are never loaded (loads are clamped to the last needed row). Only steps that
+//    reach past a wave's first position apply the element mask (key > position -> -inf).
+//  * Online softmax in base 2 (log2(e)/sqrt(dh) folded into one FMA), running max raised
+//    lazily (TSP_RESCALE_SLACK), row sums from the rounded bf16 weights (v_dot2).
 #pragma once
 
 #include "attn_common.h"
 
 namespace tsp {
 
-template <int DH, int BK>
-struct Bf16Tile {
-  static constexpr int KP = DH + 8;          // K tile row pitch (elements): conflict-free 16 B reads
-  static constexpr int VP = BK + 8;          // V^T tile row pitch (elements)
-  static constexpr int K_ELEMS = BK * KP;
-  static constexpr int V_ELEMS = DH * VP;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int K_CHUNKS = BK * DH / 8;        // 16-byte pieces of a K tile
-  static constexpr int V_GROUPS = (BK / 4) * (DH / 8);  // (4 keys x 8 dims) pieces of a V tile
-};
+typedef __bf16 tsp_bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) tsp_bf16x4* lds_bf16x4_ptr;
 
-// LDS column of the first key of 4-key group `kg` inside a V^T row. Within each block of
-// 32 keys, key 8a + 4h + b (a < 4, h < 2, b < 4) goes to column 16(a/2) + 8h + 4(a%2) + b:
-// the 8 keys a lane half h feeds to one PV MFMA step become 8 contiguous columns.
-__device__ __forceinline__ int tsp_vt_group_col(int kg) {
-  const int blk = kg >> 3, g = kg & 7, a = g >> 1, h = g & 1;
-  return blk * 32 + 16 * (a >> 1) + 8 * h + 4 * (a & 1);
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
+// operations are outstanding and leaves the LDS/export counters alone.
+__device__ __forceinline__ void tsp_wait_vmcnt(int n) {
+  switch (n) {  // the count must be an immediate
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    case 15: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+    default: __builtin_amdgcn_s_waitcnt(0x4F70); break;  // 16: vmcnt high bits = 1
+  }
 }
 
-template <int DH, int BK, int NW, int RB>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(TspParams p) {
-  using T = Bf16Tile<DH, BK>;
-  constexpr int NT = NW * 64;
-  constexpr int NKC = (T::K_CHUNKS + NT - 1) / NT;
-  constexpr int NVG = (T::V_GROUPS + NT - 1) / NT;
-  constexpr int NKB = BK / 32;  // 32-key blocks per tile
-  constexpr int NDB = DH / 32;  // 32-dim blocks of the output
-  static_assert(BK % 32 == 0 && DH % 32 == 0, "tile shape");
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// lds_addr + 16*i (gfx950 global_load_lds_dwordx4, LDS base in M0). Issued as inline
+// asm on purpose: the compiler then does not track the LDS write and does not wait for
+// every in-flight prefetch (vmcnt(0)) before each LDS read; the kernel instead waits
+// for exactly the stage it is about to read (tsp_wait_vmcnt + barrier).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void tsp_lds_dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
+__device__ __forceinline__ uint32_t tsp_lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_ptr)(p);
+}
+
+template <int DH, int NW, int NBUF>
+struct Bf16Stage {
+  static constexpr int BK = 32;                      // keys per stage (= per pipeline step)
+  static constexpr int ROW_BYTES = DH * 2;           // one K or V row
+  static constexpr int CPR = DH / 8;                 // 16-byte chunks per row
+  static constexpr int RPL = 64 / CPR;               // rows per 1 KiB wave-load
+  static constexpr int TILE_BYTES = BK * ROW_BYTES;  // one K (or V) tile of a stage
+  static constexpr int WL = TILE_BYTES / 1024;       // wave-loads per K (or V) tile
+  static constexpr int LPW = 2 * WL / NW;            // wave-loads per wave per stage
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr int PD = NBUF - 2;                // prefetch distance in stages
+  static constexpr int SWZ = CPR < 16 ? CPR : 16;    // swizzle period (chunks)
+  static_assert((2 * WL) % NW == 0, "stage loads must split evenly over the waves");
+  static_assert(LPW * PD <= 16, "vmcnt range");
+  static_assert(CPR >= 8, "head dim");
+  // XOR swizzles on the 16-byte chunk index of a row (row = key index in the stage).
+  // K: lanes reading 16 consecutive rows at one logical chunk hit 16 distinct chunks.
+  __device__ static int swz_k(int row) { return row & (SWZ - 1); }
+  // V: the transposing read takes 32 bytes (an even/odd chunk pair) from each of 4
+  // consecutive rows; an even XOR moves whole pairs, giving the 4 rows distinct pairs.
+  __device__ static int swz_v(int row) { return (2 * row) & (SWZ - 2); }
+};
+
+template <int DH, int NW, int RB, int NBUF, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p) {
+  using St = Bf16Stage<DH, NW, NBUF>;
+  constexpr int BK = St::BK;
+  constexpr int NDB = DH / 32;  // 32-dim blocks of the output
+  constexpr int NKK = DH / 16;  // reduction steps of QK^T
+  constexpr int PD = St::PD;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * St::STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int half = lane >> 5;
 
@@ -87,8 +143,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(TspParams p) {
   const int64_t kv_row_stride = (int64_t)p.Hkv * DH;  // elements between consecutive keys
   const uint16_t* __restrict__ kbase = kg + ((int64_t)b * p.S_total * p.Hkv + hk) * DH;
   const uint16_t* __restrict__ vbase = vg + ((int64_t)b * p.S_total * p.Hkv + hk) * DH;
-
   const int pos_blocks = p.BQ / 32;  // row blocks per head in a tile
+
+  // ---- per-lane LDS read offsets (constant over the sweep) ------------------------------
+  // K operand of QK^T step kk: row `col`, logical chunk 2kk + half.
+  int koff[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = col * St::ROW_BYTES + (((2 * kk + half) ^ St::swz_k(col)) << 4);
+  // V^T operand of PV block db: in each 16-lane group g, source lane s addresses row
+  // 4*half + s/4 (+16 per 16-key step, +8 for the second read) and dims
+  // db*32 + 16(g&1) + 4(s&3) .. +3; lane s then receives dim db*32 + 16(g&1) + s of the
+  // 4 rows, which is the A operand layout with keys in the P operand's order.
+  int voff[NDB];
+  {
+    const int g = lane >> 4, s = lane & 15;
+    const int vrow = 4 * half + (s >> 2);
+    const int xv = St::swz_v(vrow);  // rows +8 and +16 have the same swizzle
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int chunk = db * 4 + 2 * (g & 1) + ((s & 3) >> 1);
+      voff[db] = vrow * St::ROW_BYTES + ((chunk ^ xv) << 4) + ((s & 1) << 3);
+    }
+  }
 
   for (int which = 0; which < 2; ++which) {
     const int32_t qt = which == 0 ? p.n_qtiles - 1 - pair : pair;
@@ -101,7 +177,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(TspParams p) {
     // ---- this wave's query rows -------------------------------------------------------
     int32_t lrow[RB], qpos[RB], head[RB];
     bool rvalid[RB];
-    int32_t wave_first = 0x7fffffff, wave_last = -1;  // local rows (uniform)
+    int32_t wave_first = 0x7fffffff;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int rbi = wave * RB + rb;
@@ -112,19 +188,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(TspParams p) {
       lrow[rb] = min(r, p.S_local - 1);
       qpos[rb] = tsp_zigzag_position(lrow[rb], p.C, p.D, p.rank);
       wave_first = min(wave_first, row0 + pb * 32);
-      wave_last = max(wave_last, min(row0 + pb * 32 + 31, p.S_local - 1));
     }
-    const bool wave_active = wave_first < p.S_local;
     const int32_t wave_min_pos = tsp_zigzag_position(min(wave_first, p.S_local - 1), p.C, p.D, p.rank);
-    const int32_t wave_max_pos = tsp_zigzag_position(wave_last, p.C, p.D, p.rank);
+    // steps [0, t_mask) are visible to every row of the wave; later steps are masked
+    const int32_t t_mask = min(n_kv, (wave_min_pos + 1) / BK);
 
-    // ---- Q^T operands stay in registers for the whole sweep -----------------------------
-    tsp_bf16x8 qf[RB][DH / 16];
+    // ---- Q^T operands stay in registers ------------------------------------------------
+    tsp_bf16x8 qf[RB][NKK];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const uint16_t* qp = qg + (((int64_t)b * p.S_local + lrow[rb]) * p.Hq + head[rb]) * DH + half * 8;
 #pragma unroll
-      for (int kk = 0; kk < DH / 16; ++kk)
+      for (int kk = 0; kk < NKK; ++kk)
         qf[rb][kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(qp + kk * 16));
     }
 
@@ -140,195 +215,200 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(TspParams p) {
         for (int e = 0; e < 16; ++e) acc[rb][db][e] = 0.f;
     }
 
-    // ---- staging of one K/V tile: global -> registers -> LDS ----------------------------
-    tsp_u32x4 kreg[NKC];
-    tsp_u32x4 vreg[NVG][4];
-    auto load_tile = [&](int j) {
-      const int32_t kv0 = j * BK;
+    // ---- stage loads: global -> LDS, this wave's share --------------------------------
+    auto issue_stage = [&](int s) {
+      const int32_t kv0 = s * BK;
+      uint8_t* sb = smem + (s % NBUF) * St::STAGE_BYTES;
 #pragma unroll
-      for (int it = 0; it < NKC; ++it) {
-        const int c = tid + it * NT;
-        const int row = c / (DH / 8), c8 = c % (DH / 8);
-        const int32_t key = kv0 + row;
-        tsp_u32x4 z = {0u, 0u, 0u, 0u};
-        if ((T::K_CHUNKS % NT == 0 || c < T::K_CHUNKS) && key < kv_end)
-          z = *reinterpret_cast<const tsp_u32x4*>(kbase + key * kv_row_stride + c8 * 8);
-        kreg[it] = z;
-      }
-#pragma unroll
-      for (int it = 0; it < NVG; ++it) {
-        const int g = tid + it * NT;
-        const int kgp = g % (BK / 4), dc = g / (BK / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int32_t key = kv0 + kgp * 4 + r;
-          tsp_u32x4 z = {0u, 0u, 0u, 0u};
-          if ((T::V_GROUPS % NT == 0 || g < T::V_GROUPS) && key < kv_end)
-            z = *reinterpret_cast<const tsp_u32x4*>(vbase + key * kv_row_stride + dc * 8);
-          vreg[it][r] = z;
-        }
+      for (int q = 0; q < St::LPW; ++q) {
+        const int i = wave * St::LPW + q;  // wave-load index in the stage (uniform)
+        const bool isv = i >= St::WL;
+        const int j = isv ? i - St::WL : i;
+        const int row = j * St::RPL + lane / St::CPR;
+        const int c = (lane % St::CPR) ^ (isv ? St::swz_v(row) : St::swz_k(row));
+        const int32_t key = min(kv0 + row, kv_end - 1);
+        const uint16_t* src = (isv ? vbase : kbase) + key * kv_row_stride + c * 8;
+        tsp_lds_dma16(src, __builtin_amdgcn_readfirstlane(tsp_lds_addr(sb + (isv ? St::TILE_BYTES : 0) + j * 1024)));
       }
     };
-    auto store_tile = [&](int buf) {
-      uint16_t* sk = smem + buf * T::STAGE;
-      uint16_t* sv = sk + T::K_ELEMS;
-#pragma unroll
-      for (int it = 0; it < NKC; ++it) {
-        const int c = tid + it * NT;
-        if (T::K_CHUNKS % NT == 0 || c < T::K_CHUNKS) {
-          const int row = c / (DH / 8), c8 = c % (DH / 8);
-          *reinterpret_cast<tsp_u32x4*>(sk + row * T::KP + c8 * 8) = kreg[it];
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < NVG; ++it) {
-        const int g = tid + it * NT;
-        if (T::V_GROUPS % NT == 0 || g < T::V_GROUPS) {
-          const int kgp = g % (BK / 4), dc = g / (BK / 4);
-          const int colv = tsp_vt_group_col(kgp);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const int w = c >> 1;
-            uint32_t x0 = vreg[it][0][w], x1 = vreg[it][1][w], x2 = vreg[it][2][w], x3 = vreg[it][3][w];
-            tsp_u32x2 pk;
-            if (c & 1) {
-              pk[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-              pk[1] = (x2 >> 16) | (x3 & 0xffff0000u);
-            } else {
-              pk[0] = (x0 & 0xffffu) | (x1 << 16);
-              pk[1] = (x2 & 0xffffu) | (x3 << 16);
-            }
-            *reinterpret_cast<tsp_u32x2*>(sv + (dc * 8 + c) * T::VP + colv) = pk;
-          }
-        }
-      }
+    // Wait until stage s has landed for every wave; the stages issued after it (up to
+    // last_issued) stay in flight.
+    auto stage_ready = [&](int s, int last_issued) {
+      tsp_wait_vmcnt(St::LPW * (last_issued - s));
+      __syncthreads();
     };
 
-    __syncthreads();  // the previous tile's last readers are done with both buffers
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int j = 0; j < n_kv; ++j) {
-      const bool more = j + 1 < n_kv;
-      if (more) load_tile(j + 1);
-      const int32_t kv0 = j * BK;
-
-      if (wave_active && kv0 <= wave_max_pos) {
-        const uint16_t* sk = smem + (j & 1) * T::STAGE;
-        const uint16_t* sv = sk + T::K_ELEMS;
-
-        // S^T = K Q^T for this tile: NKB blocks of 32 keys x 32 queries per row block.
-        tsp_f32x16 s[RB][NKB];
+    // ---- pipeline pieces ---------------------------------------------------------------
+    auto qk = [&](int s, tsp_f32x16(&sc)[RB]) {
+      const uint8_t* kt = smem + (s % NBUF) * St::STAGE_BYTES;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[rb][e] = 0.f;
+      tsp_bf16x8 kf[NKK];  // all K operands of the step in flight before the first MFMA
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        kf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(kt + koff[kk]));
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
+          sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[rb][kk], sc[rb], 0, 0, 0);
+    };
+    // key s*BK + 8(e/4) + 4*half + (e%4) of query column `col` is visible iff <= qpos
+    auto mask = [&](int s, tsp_f32x16(&sc)[RB]) {
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
+      for (int rb = 0; rb < RB; ++rb) {
+        const int32_t lim = qpos[rb] - s * BK - 4 * half;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) s[rb][kb][e] = 0.f;
+        for (int e = 0; e < 16; ++e)
+          if ((8 * (e >> 2) + (e & 3)) > lim) sc[rb][e] = -INFINITY;
+      }
+    };
+    auto rowmax = [&](const tsp_f32x16(&sc)[RB], float(&mx)[RB]) {
 #pragma unroll
-        for (int kk = 0; kk < DH / 16; ++kk) {
+      for (int rb = 0; rb < RB; ++rb) {
+        float m = sc[rb][0];
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            const tsp_bf16x8 kf = __builtin_bit_cast(
-                tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(sk + (kb * 32 + col) * T::KP + kk * 16 + half * 8));
+        for (int e = 1; e < 16; ++e) m = fmaxf(m, sc[rb][e]);
+        mx[rb] = tsp_max_halves(m) * p.scale_log2;
+      }
+    };
+    auto rescale_needed = [&](const float(&mx)[RB]) {
+      bool need = false;
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][kk], s[rb][kb], 0, 0, 0);
-          }
+      for (int rb = 0; rb < RB; ++rb) need |= mx[rb] > m_run[rb] + TSP_RESCALE_SLACK;
+      return __builtin_amdgcn_ballot_w64(need) != 0;  // wave-uniform
+    };
+    // Raise the running max to cover this step (rare after the first step): scale the
+    // accumulated output and sum by 2^(m_old - m_new).
+    auto rescale = [&](const float(&mx)[RB]) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float m_new = fmaxf(m_run[rb], mx[rb]);
+        const float alpha = tsp_exp2(m_run[rb] - m_new);
+        m_run[rb] = m_new;
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[rb][db][e] *= alpha;
+      }
+    };
+    auto softmax = [&](const tsp_f32x16(&sc)[RB], tsp_bf16x8(&pf)[RB][2]) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float mneg = -m_run[rb];
+        float lsum = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          float pw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pw[e] = tsp_exp2(fmaf(sc[rb][st * 8 + e], p.scale_log2, mneg));
+          tsp_u32x4 w;
+          w[0] = tsp_pack_bf16(pw[0], pw[1]);
+          w[1] = tsp_pack_bf16(pw[2], pw[3]);
+          w[2] = tsp_pack_bf16(pw[4], pw[5]);
+          w[3] = tsp_pack_bf16(pw[6], pw[7]);
+          // the row sum uses the rounded weights the PV product applies
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lsum = tsp_sum_bf16_pair(w[e], lsum);
+          pf[rb][st] = __builtin_bit_cast(tsp_bf16x8, w);
         }
-
-        // Mask, online softmax, P^T operands.
-        const bool need_mask = kv0 + BK - 1 > wave_min_pos;
-        tsp_bf16x8 pf[RB][BK / 16];
-    #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-          // lane holds keys kv0 + 32kb + 8(e/4) + 4*half + (e%4) of query column `col`
-          const int32_t lim = qpos[rb] - kv0 - 4 * half;
-          float mx = -INFINITY;
+        l_run[rb] += lsum;
+      }
+    };
+    auto pv = [&](int s, const tsp_bf16x8(&pf)[RB][2]) {
+      const uint8_t* vt = smem + (s % NBUF) * St::STAGE_BYTES + St::TILE_BYTES;
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
+      for (int st = 0; st < 2; ++st) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              float x = s[rb][kb][e];
-              if (need_mask && (kb * 32 + 8 * (e >> 2) + (e & 3)) > lim) x = -INFINITY;
-              s[rb][kb][e] = x;
-              mx = fmaxf(mx, x);
-            }
-          mx = tsp_max_halves(mx);
-          const float mt = mx * p.scale_log2;
-          if (__builtin_amdgcn_ballot_w64(mt > m_run[rb] + TSP_RESCALE_SLACK) != 0) {
-            const float m_new = fmaxf(m_run[rb], mt);
-            const float alpha = tsp_exp2(m_run[rb] - m_new);
-            m_run[rb] = m_new;
-            l_run[rb] *= alpha;
+        for (int db = 0; db < NDB; ++db) {
+          const uint8_t* a = vt + voff[db] + st * 16 * St::ROW_BYTES;
+          const tsp_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a));
+          const tsp_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a + 8 * St::ROW_BYTES));
+          const tsp_bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) acc[rb][db][e] *= alpha;
-          }
-          const float mneg = -m_run[rb];
-          float lsum = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-              float pv[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) pv[e] = tsp_exp2(fmaf(s[rb][kb][st * 8 + e], p.scale_log2, mneg));
-              tsp_u32x4 w;
-              w[0] = tsp_pack_bf16(pv[0], pv[1]);
-              w[1] = tsp_pack_bf16(pv[2], pv[3]);
-              w[2] = tsp_pack_bf16(pv[4], pv[5]);
-              w[3] = tsp_pack_bf16(pv[6], pv[7]);
-              // the row sum uses the rounded weights the PV product applies
-#pragma unroll
-              for (int e = 0; e < 4; ++e) lsum = tsp_sum_bf16_pair(w[e], lsum);
-              pf[rb][kb * 2 + st] = __builtin_bit_cast(tsp_bf16x8, w);
-            }
-          }
-          l_run[rb] += lsum;
-        }
-
-        // O^T += V^T P^T
-#pragma unroll
-        for (int st = 0; st < BK / 16; ++st) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const tsp_bf16x8 vf = __builtin_bit_cast(
-                tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(sv + (db * 32 + col) * T::VP + st * 16 + half * 8));
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb][st], acc[rb][db], 0, 0, 0);
-          }
+          for (int rb = 0; rb < RB; ++rb)
+            acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb][st], acc[rb][db], 0, 0, 0);
         }
       }
+    };
 
-      if (more) store_tile((j + 1) & 1);
-      __syncthreads();
+    // ---- prologue -------------------------------------------------------------------
+    __syncthreads();  // the previous tile's readers are done with every buffer
+    const int pro = min(PD, n_kv - 1);
+    for (int s = 0; s <= pro; ++s) issue_stage(s);
+    int issued = pro;  // last stage issued
+    stage_ready(0, issued);
+
+    tsp_f32x16 s_cur[RB];
+    float mx[RB];
+    qk(0, s_cur);
+    if (t_mask == 0) mask(0, s_cur);
+    rowmax(s_cur, mx);
+
+    // One pipelined step: scores of step t+1 on the matrix pipe while the vector pipe
+    // turns step t's scores into weights; then step t's PV while step t+1's row max runs.
+    tsp_f32x16 s_nxt[RB];
+    auto step = [&](int t, bool mask_next) {
+      tsp_bf16x8 pf[RB][2];
+      stage_ready(t + 1, issued);
+      if (issued + 1 < n_kv) issue_stage(++issued);
+      qk(t + 1, s_nxt);
+      softmax(s_cur, pf);
+      pv(t, pf);
+      if (mask_next) mask(t + 1, s_nxt);
+      rowmax(s_nxt, mx);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_nxt[rb];
+    };
+
+    // ---- main sweep ----------------------------------------------------------------------
+    // Hot loop: steps whose successor needs no mask and which need no rescale. A rescale
+    // leaves the loop, is applied out of line, and the sweep resumes.
+    int t = 0;
+    while (t + 1 < t_mask) {
+      for (; t + 1 < t_mask; ++t) {
+        if (rescale_needed(mx)) break;
+        step(t, false);
+      }
+      if (t + 1 >= t_mask) break;
+      rescale(mx);
+      step(t, false);
+      ++t;
+    }
+    // Tail: the masked steps near the diagonal (and the last step).
+    for (; t < n_kv; ++t) {
+      if (rescale_needed(mx)) rescale(mx);
+      if (t + 1 < n_kv) {
+        step(t, true);
+      } else {
+        tsp_bf16x8 pf[RB][2];
+        softmax(s_cur, pf);
+        pv(t, pf);
+      }
     }
 
     // ---- epilogue: normalise, round to bf16, write O and lse -----------------------------
-    if (wave_active) {
-  #pragma unroll
+#pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const float l = tsp_sum_halves(l_run[rb]);
-        const float inv = 1.0f / l;
-        if (rvalid[rb]) {
-          uint16_t* op = og + (((int64_t)b * p.S_local + lrow[rb]) * p.Hq + head[rb]) * DH + 4 * half;
+      const float l = tsp_sum_halves(l_run[rb]);
+      const float inv = 1.0f / l;
+      if (rvalid[rb]) {
+        uint16_t* op = og + (((int64_t)b * p.S_local + lrow[rb]) * p.Hq + head[rb]) * DH + 4 * half;
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              tsp_u32x2 w;
-              w[0] = tsp_pack_bf16(acc[rb][db][4 * a + 0] * inv, acc[rb][db][4 * a + 1] * inv);
-              w[1] = tsp_pack_bf16(acc[rb][db][4 * a + 2] * inv, acc[rb][db][4 * a + 3] * inv);
-              *reinterpret_cast<tsp_u32x2*>(op + db * 32 + 8 * a) = w;
-            }
-          if (half == 0)
-            p.lse[((int64_t)b * p.Hq + head[rb]) * p.S_local + lrow[rb]] =
-                (m_run[rb] + __builtin_amdgcn_logf(l)) * TSP_LN2;
-        }
+          for (int a = 0; a < 4; ++a) {
+            tsp_u32x2 w;
+            w[0] = tsp_pack_bf16(acc[rb][db][4 * a + 0] * inv, acc[rb][db][4 * a + 1] * inv);
+            w[1] = tsp_pack_bf16(acc[rb][db][4 * a + 2] * inv, acc[rb][db][4 * a + 3] * inv);
+            *reinterpret_cast<tsp_u32x2*>(op + db * 32 + 8 * a) = w;
+          }
+        if (half == 0)
+          p.lse[((int64_t)b * p.Hq + head[rb]) * p.S_local + lrow[rb]] =
+              (m_run[rb] + __builtin_amdgcn_logf(l)) * TSP_LN2;
       }
     }
   }

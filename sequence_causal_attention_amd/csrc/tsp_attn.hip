@@ -28,6 +28,29 @@ int fail(int status, const char* fmt, ...) {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+// Tile configuration of the bf16 kernels per head dim: waves per workgroup, 32-row query
+// blocks per wave, depth of the LDS stage ring, target waves per SIMD.
+#ifndef TSP_DH128_NW
+#define TSP_DH128_NW 8
+#endif
+#ifndef TSP_DH128_NBUF
+#define TSP_DH128_NBUF 4
+#endif
+template <int DH>
+struct Bf16Cfg;
+template <>
+struct Bf16Cfg<64> {
+  static constexpr int NW = 4, RB = 2, NBUF = 6, OCC = 1;
+};
+template <>
+struct Bf16Cfg<128> {
+  static constexpr int NW = TSP_DH128_NW, RB = 1, NBUF = TSP_DH128_NBUF, OCC = 2;
+};
+template <>
+struct Bf16Cfg<256> {
+  static constexpr int NW = 4, RB = 1, NBUF = 4, OCC = 1;
+};
+
 // Tile configuration of one (dtype, dh) kernel.
 struct KernelShape {
   int kv_tile;     // keys per K/V tile
@@ -35,13 +58,21 @@ struct KernelShape {
   int row_blocks;  // 32-row query blocks per wave
 };
 
+template <int DH>
+KernelShape bf16_shape() {
+  return KernelShape{tsp::Bf16Stage<DH, Bf16Cfg<DH>::NW, Bf16Cfg<DH>::NBUF>::BK, Bf16Cfg<DH>::NW, Bf16Cfg<DH>::RB};
+}
+
 bool kernel_shape(int dtype, int64_t dh, KernelShape* ks) {
-  if (dh != 64 && dh != 128 && dh != 256) return false;
   if (dtype == TSP_BF16) {
-    *ks = KernelShape{dh == 256 ? 32 : 64, 4, 1};
-    return true;
+    switch (dh) {
+      case 64: *ks = bf16_shape<64>(); return true;
+      case 128: *ks = bf16_shape<128>(); return true;
+      case 256: *ks = bf16_shape<256>(); return true;
+    }
+    return false;
   }
-  if (dtype == TSP_F32) {
+  if (dtype == TSP_F32 && (dh == 64 || dh == 128 || dh == 256)) {
     *ks = KernelShape{32, 4, 1};
     return true;
   }
@@ -102,9 +133,11 @@ int plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_
   return TSP_OK;
 }
 
-template <int DH, int BK, int NW, int RB>
+template <int DH>
 void launch_bf16(const TspParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, BK, NW, RB>), dim3(p.n_units), dim3(NW * 64), 0, stream, p);
+  using C = Bf16Cfg<DH>;
+  hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::OCC>), dim3(p.n_units), dim3(C::NW * 64),
+                     0, stream, p);
 }
 
 template <int DH>
@@ -140,9 +173,9 @@ int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, vo
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
   if (dtype == TSP_BF16) {
     switch (dh) {
-      case 64: launch_bf16<64, 64, 4, 1>(p, s); break;
-      case 128: launch_bf16<128, 64, 4, 1>(p, s); break;
-      case 256: launch_bf16<256, 32, 4, 1>(p, s); break;
+      case 64: launch_bf16<64>(p, s); break;
+      case 128: launch_bf16<128>(p, s); break;
+      case 256: launch_bf16<256>(p, s); break;
     }
   } else {
     switch (dh) {
