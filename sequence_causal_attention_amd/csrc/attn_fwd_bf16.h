@@ -36,6 +36,8 @@
 //    lazily (TSP_RESCALE_SLACK), row sums from the rounded bf16 weights (v_dot2).
 #pragma once
 
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace tsp {
@@ -166,6 +168,26 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     }
   }
 
+  // ---- this wave's share of every stage load (constant over the sweep) ------------------
+  // Load q of a stage moves 1 KiB: K rows (first WL loads) or V rows (next WL), lane i
+  // landing at byte 16*i of the load's slot; row and swizzled chunk depend only on the lane.
+  const int64_t stage_stride = (int64_t)BK * kv_row_stride;  // elements from one stage to the next
+  const uint16_t* dma_src[St::LPW];  // stage-0 source of each load (no clamp)
+  int dma_row[St::LPW];              // key row of each load within a stage
+  uint32_t dma_slot[St::LPW];        // LDS byte offset of each load within a stage
+#pragma unroll
+  for (int q = 0; q < St::LPW; ++q) {
+    const int i = wave * St::LPW + q;
+    const bool isv = i >= St::WL;
+    const int j = isv ? i - St::WL : i;
+    const int row = j * St::RPL + lane / St::CPR;
+    const int c = (lane % St::CPR) ^ (isv ? St::swz_v(row) : St::swz_k(row));
+    dma_row[q] = row;
+    dma_src[q] = (isv ? vbase : kbase) + row * kv_row_stride + c * 8;
+    dma_slot[q] = (isv ? St::TILE_BYTES : 0) + j * 1024;
+  }
+  const uint32_t smem_addr = __builtin_amdgcn_readfirstlane(tsp_lds_addr(smem));
+
   for (int which = 0; which < 2; ++which) {
     const int32_t qt = which == 0 ? p.n_qtiles - 1 - pair : pair;
     if (which == 1 && qt == p.n_qtiles - 1 - pair) break;  // middle tile of an odd count
@@ -216,19 +238,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     }
 
     // ---- stage loads: global -> LDS, this wave's share --------------------------------
+    // Any stage: rows past the tile's last position are clamped to it (never read past it).
     auto issue_stage = [&](int s) {
       const int32_t kv0 = s * BK;
-      uint8_t* sb = smem + (s % NBUF) * St::STAGE_BYTES;
+      const uint32_t base = smem_addr + (s % NBUF) * St::STAGE_BYTES;
 #pragma unroll
       for (int q = 0; q < St::LPW; ++q) {
-        const int i = wave * St::LPW + q;  // wave-load index in the stage (uniform)
-        const bool isv = i >= St::WL;
-        const int j = isv ? i - St::WL : i;
-        const int row = j * St::RPL + lane / St::CPR;
-        const int c = (lane % St::CPR) ^ (isv ? St::swz_v(row) : St::swz_k(row));
-        const int32_t key = min(kv0 + row, kv_end - 1);
-        const uint16_t* src = (isv ? vbase : kbase) + key * kv_row_stride + c * 8;
-        tsp_lds_dma16(src, __builtin_amdgcn_readfirstlane(tsp_lds_addr(sb + (isv ? St::TILE_BYTES : 0) + j * 1024)));
+        const int32_t over = max(0, kv0 + dma_row[q] - (kv_end - 1));  // rows beyond the last key
+        tsp_lds_dma16(dma_src[q] + (int64_t)(kv0 - over) * kv_row_stride, base + dma_slot[q]);
       }
     };
     // Wait until stage s has landed for every wave; the stages issued after it (up to
@@ -339,8 +356,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     __syncthreads();  // the previous tile's readers are done with every buffer
     const int pro = min(PD, n_kv - 1);
     for (int s = 0; s <= pro; ++s) issue_stage(s);
-    int issued = pro;  // last stage issued
-    stage_ready(0, issued);
+    stage_ready(0, pro);
 
     tsp_f32x16 s_cur[RB];
     float mx[RB];
@@ -348,43 +364,57 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     if (t_mask == 0) mask(0, s_cur);
     rowmax(s_cur, mx);
 
-    // One pipelined step: scores of step t+1 on the matrix pipe while the vector pipe
-    // turns step t's scores into weights; then step t's PV while step t+1's row max runs.
-    tsp_f32x16 s_nxt[RB];
-    auto step = [&](int t, bool mask_next) {
-      tsp_bf16x8 pf[RB][2];
-      stage_ready(t + 1, issued);
-      if (issued + 1 < n_kv) issue_stage(++issued);
-      qk(t + 1, s_nxt);
-      softmax(s_cur, pf);
-      pv(t, pf);
-      if (mask_next) mask(t + 1, s_nxt);
-      rowmax(s_nxt, mx);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_nxt[rb];
-    };
-
     // ---- main sweep ----------------------------------------------------------------------
-    // Hot loop: steps whose successor needs no mask and which need no rescale. A rescale
-    // leaves the loop, is applied out of line, and the sweep resumes.
-    int t = 0;
-    while (t + 1 < t_mask) {
-      for (; t + 1 < t_mask; ++t) {
-        if (rescale_needed(mx)) break;
-        step(t, false);
+    // Fast path: steps whose successor needs no mask and whose prefetch stage lies fully
+    // below kv_end. Unrolled by the ring depth so every LDS slot is a compile-time offset
+    // and the two score tiles alternate without copies; constant vmcnt; no clamping.
+    static_assert(NBUF == 4, "the fast path is unrolled by a ring of 4 stages");
+    constexpr int VM_STEADY = St::LPW * (PD - 1);
+    const int32_t n_full = kv_end / BK;  // stages with every key below kv_end
+    const int t_fast = min(t_mask - 1, n_full - 1 - PD);
+    tsp_f32x16 s_alt[RB];
+    auto fast_step = [&](auto u_const, int t, tsp_f32x16(&sc)[RB], tsp_f32x16(&sn)[RB]) {
+      constexpr int U = decltype(u_const)::value;  // t % 4
+      if (rescale_needed(mx)) rescale(mx);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // stage t+1 landed (this wave's part)
+      __syncthreads();                                 // ... for every wave; slot (t-1)%4 free
+      {
+        const int64_t adv = (int64_t)(t + 1 + PD) * stage_stride;
+        const uint32_t base = smem_addr + ((U + 1 + PD) % NBUF) * St::STAGE_BYTES;
+#pragma unroll
+        for (int q = 0; q < St::LPW; ++q) tsp_lds_dma16(dma_src[q] + adv, base + dma_slot[q]);
       }
-      if (t + 1 >= t_mask) break;
-      rescale(mx);
-      step(t, false);
-      ++t;
+      tsp_bf16x8 pf[RB][2];
+      qk((U + 1) % NBUF, sn);  // matrix pipe: next step's scores
+      softmax(sc, pf);         // vector pipe: this step's weights
+      pv(U % NBUF, pf);        // matrix pipe: this step's output
+      rowmax(sn, mx);          // vector pipe: next step's row max
+    };
+    int t = 0;
+    for (; t + 4 <= t_fast; t += 4) {
+      fast_step(std::integral_constant<int, 0>{}, t + 0, s_cur, s_alt);
+      fast_step(std::integral_constant<int, 1>{}, t + 1, s_alt, s_cur);
+      fast_step(std::integral_constant<int, 2>{}, t + 2, s_cur, s_alt);
+      fast_step(std::integral_constant<int, 3>{}, t + 3, s_alt, s_cur);
     }
-    // Tail: the masked steps near the diagonal (and the last step).
+    int issued = t > 0 ? t + PD : pro;  // last stage issued so far
+
+    // General path: the masked steps near the diagonal, the partial last stage and the
+    // ring drain.
     for (; t < n_kv; ++t) {
       if (rescale_needed(mx)) rescale(mx);
+      tsp_bf16x8 pf[RB][2];
       if (t + 1 < n_kv) {
-        step(t, true);
+        stage_ready(t + 1, issued);
+        if (issued + 1 < n_kv) issue_stage(++issued);
+        qk(t + 1, s_alt);
+        softmax(s_cur, pf);
+        pv(t, pf);
+        if (t + 1 >= t_mask) mask(t + 1, s_alt);
+        rowmax(s_alt, mx);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_alt[rb];
       } else {
-        tsp_bf16x8 pf[RB][2];
         softmax(s_cur, pf);
         pv(t, pf);
       }

@@ -40,7 +40,7 @@ template <int DH>
 struct Bf16Cfg;
 template <>
 struct Bf16Cfg<64> {
-  static constexpr int NW = 4, RB = 2, NBUF = 6, OCC = 1;
+  static constexpr int NW = 4, RB = 2, NBUF = 4, OCC = 1;
 };
 template <>
 struct Bf16Cfg<128> {
