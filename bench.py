@@ -98,6 +98,9 @@ def main():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run plain device copies of MIB MiB (the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -109,6 +112,16 @@ def main():
 
     import sequence_causal_attention_amd as tsp
     import workloads
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.randn(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": max(1, args.steps)}), flush=True)
+        return
 
     w = workloads.BY_NAME[args.workload]
     rank = w.ranks[0] if args.rank is None else args.rank
