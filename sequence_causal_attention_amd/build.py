@@ -33,7 +33,7 @@ def command(out: str = LIB, extra=()) -> list:
         hipcc(),
         "--offload-arch=gfx950",
         "-O3",
-        "-std=c++17",
+        "-std=c++20",
         "-fPIC",
         "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -70,17 +70,18 @@ __device__ __forceinline__ void tsp_wait_vmcnt(int n) {
   }
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane i writes
-// lds_addr + 16*i (gfx950 global_load_lds_dwordx4, LDS base in M0). Issued as inline
-// asm on purpose: the compiler then does not track the LDS write and does not wait for
-// every in-flight prefetch (vmcnt(0)) before each LDS read; the kernel instead waits
-// for exactly the stage it is about to read (tsp_wait_vmcnt + barrier).
+// 16 bytes per lane from global memory straight into LDS: lane i reads sbase + voff
+// (sbase wave-uniform, voff its own byte offset) and writes lds_addr + 16*i (gfx950
+// global_load_lds_dwordx4, saddr form, LDS base in M0). Issued as inline asm on purpose:
+// the compiler then does not track the LDS write and does not wait for every in-flight
+// prefetch (vmcnt(0)) before each LDS read; the kernel instead waits for exactly the
+// stage it is about to read (vmcnt + barrier).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void tsp_lds_dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+__device__ __forceinline__ void tsp_lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(src), "s"(lds_addr)
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -89,13 +90,14 @@ __device__ __forceinline__ uint32_t tsp_lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_ptr)(p);
 }
 
-template <int DH, int NW, int NBUF>
+template <int DH, int NW, int NBUF, int SPS>
 struct Bf16Stage {
-  static constexpr int BK = 32;                      // keys per stage (= per pipeline step)
-  static constexpr int ROW_BYTES = DH * 2;           // one K or V row
-  static constexpr int CPR = DH / 8;                 // 16-byte chunks per row
-  static constexpr int RPL = 64 / CPR;               // rows per 1 KiB wave-load
-  static constexpr int TILE_BYTES = BK * ROW_BYTES;  // one K (or V) tile of a stage
+  static constexpr int BK = 32;                       // keys per pipeline step
+  static constexpr int BKS = BK * SPS;                // keys per stage (one wait + barrier)
+  static constexpr int ROW_BYTES = DH * 2;            // one K or V row
+  static constexpr int CPR = DH / 8;                  // 16-byte chunks per row
+  static constexpr int RPL = 64 / CPR;                // rows per 1 KiB wave-load
+  static constexpr int TILE_BYTES = BKS * ROW_BYTES;  // one K (or V) tile of a stage
   static constexpr int WL = TILE_BYTES / 1024;       // wave-loads per K (or V) tile
   static constexpr int LPW = 2 * WL / NW;            // wave-loads per wave per stage
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
@@ -107,14 +109,17 @@ struct Bf16Stage {
   // XOR swizzles on the 16-byte chunk index of a row (row = key index in the stage).
   // K: lanes reading 16 consecutive rows at one logical chunk hit 16 distinct chunks.
   __device__ static int swz_k(int row) { return row & (SWZ - 1); }
-  // V: the transposing read takes 32 bytes (an even/odd chunk pair) from each of 4
-  // consecutive rows; an even XOR moves whole pairs, giving the 4 rows distinct pairs.
-  __device__ static int swz_v(int row) { return (2 * row) & (SWZ - 2); }
+  // V: a 16-lane group of the transposing read takes one chunk pair (32 bytes) from each
+  // of 4 consecutive rows, and the next group the adjacent pair of the same rows. XOR-ing
+  // the chunk index with 4*(row%4) keeps pairs whole and spreads those 8 (row, pair)
+  // reads over 8 distinct 32-byte bank groups. With 128-byte rows (dh 64) two rows share
+  // one 256-byte bank line, so the row's second bit picks the XOR instead.
+  __device__ static int swz_v(int row) { return CPR >= 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 };
 
-template <int DH, int NW, int RB, int NBUF, int OCC>
+template <int DH, int NW, int RB, int NBUF, int SPS, int OCC>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p) {
-  using St = Bf16Stage<DH, NW, NBUF>;
+  using St = Bf16Stage<DH, NW, NBUF, SPS>;
   constexpr int BK = St::BK;
   constexpr int NDB = DH / 32;  // 32-dim blocks of the output
   constexpr int NKK = DH / 16;  // reduction steps of QK^T
@@ -169,21 +174,27 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
   }
 
   // ---- this wave's share of every stage load (constant over the sweep) ------------------
-  // Load q of a stage moves 1 KiB: K rows (first WL loads) or V rows (next WL), lane i
-  // landing at byte 16*i of the load's slot; row and swizzled chunk depend only on the lane.
-  const int64_t stage_stride = (int64_t)BK * kv_row_stride;  // elements from one stage to the next
-  const uint16_t* dma_src[St::LPW];  // stage-0 source of each load (no clamp)
-  int dma_row[St::LPW];              // key row of each load within a stage
-  uint32_t dma_slot[St::LPW];        // LDS byte offset of each load within a stage
+  // A stage is WL 1-KiB loads of K rows followed by WL of V rows; load i = q*NW + wave is
+  // this wave's q-th. Lane l of a load lands at byte 16*l of the load's LDS slot, which is
+  // stage row j*RPL + l/CPR, physical chunk l%CPR; it fetches the row's logical chunk
+  // (physical ^ swizzle) from global memory. The byte offset from the tensor base of the
+  // stage depends only on the lane and q.
+  const int64_t stage_stride = (int64_t)St::BKS * kv_row_stride;  // elements from one stage to the next
+  const int64_t row_bytes_g = kv_row_stride * 2;                  // bytes between consecutive keys
+  uint32_t dma_voff[St::LPW];  // per-lane byte offset of each load at stage 0
+  int dma_row[St::LPW];        // its key row within a stage
+  bool dma_isv[St::LPW];       // V (else K) load (wave-uniform)
+  uint32_t dma_slot[St::LPW];  // LDS byte offset of the load within a stage (wave-uniform)
 #pragma unroll
   for (int q = 0; q < St::LPW; ++q) {
-    const int i = wave * St::LPW + q;
+    const int i = q * NW + wave;
     const bool isv = i >= St::WL;
     const int j = isv ? i - St::WL : i;
     const int row = j * St::RPL + lane / St::CPR;
     const int c = (lane % St::CPR) ^ (isv ? St::swz_v(row) : St::swz_k(row));
     dma_row[q] = row;
-    dma_src[q] = (isv ? vbase : kbase) + row * kv_row_stride + c * 8;
+    dma_isv[q] = isv;
+    dma_voff[q] = (uint32_t)(row * row_bytes_g + c * 16);
     dma_slot[q] = (isv ? St::TILE_BYTES : 0) + j * 1024;
   }
   const uint32_t smem_addr = __builtin_amdgcn_readfirstlane(tsp_lds_addr(smem));
@@ -194,7 +205,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     const int32_t row0 = qt * p.BQ;
     const int32_t last_row = min(row0 + p.BQ, p.S_local) - 1;
     const int32_t kv_end = tsp_zigzag_position(last_row, p.C, p.D, p.rank) + 1;
-    const int32_t n_kv = (kv_end + BK - 1) / BK;
+    const int32_t n_kv = (kv_end + BK - 1) / BK;             // pipeline steps
+    const int32_t n_stage = (kv_end + St::BKS - 1) / St::BKS;  // stages
 
     // ---- this wave's query rows -------------------------------------------------------
     int32_t lrow[RB], qpos[RB], head[RB];
@@ -240,12 +252,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     // ---- stage loads: global -> LDS, this wave's share --------------------------------
     // Any stage: rows past the tile's last position are clamped to it (never read past it).
     auto issue_stage = [&](int s) {
-      const int32_t kv0 = s * BK;
+      const int32_t kv0 = s * St::BKS;
       const uint32_t base = smem_addr + (s % NBUF) * St::STAGE_BYTES;
 #pragma unroll
       for (int q = 0; q < St::LPW; ++q) {
         const int32_t over = max(0, kv0 + dma_row[q] - (kv_end - 1));  // rows beyond the last key
-        tsp_lds_dma16(dma_src[q] + (int64_t)(kv0 - over) * kv_row_stride, base + dma_slot[q]);
+        const uint16_t* tb = (dma_isv[q] ? vbase : kbase) + (int64_t)kv0 * kv_row_stride;
+        tsp_lds_dma16(tb, dma_voff[q] - (uint32_t)(over * row_bytes_g), base + dma_slot[q]);
       }
     };
     // Wait until stage s has landed for every wave; the stages issued after it (up to
@@ -256,8 +269,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     };
 
     // ---- pipeline pieces ---------------------------------------------------------------
-    auto qk = [&](int s, tsp_f32x16(&sc)[RB]) {
-      const uint8_t* kt = smem + (s % NBUF) * St::STAGE_BYTES;
+    // step t reads keys [32t, 32t+32): stage t/SPS, rows 32*(t%SPS) .. of its slot
+    auto qk = [&](int t, tsp_f32x16(&sc)[RB]) {
+      const uint8_t* kt = smem + ((t / SPS) % NBUF) * St::STAGE_BYTES + (t % SPS) * BK * St::ROW_BYTES;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -335,8 +349,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
         l_run[rb] += lsum;
       }
     };
-    auto pv = [&](int s, const tsp_bf16x8(&pf)[RB][2]) {
-      const uint8_t* vt = smem + (s % NBUF) * St::STAGE_BYTES + St::TILE_BYTES;
+    auto pv = [&](int t, const tsp_bf16x8(&pf)[RB][2]) {
+      const uint8_t* vt =
+          smem + ((t / SPS) % NBUF) * St::STAGE_BYTES + St::TILE_BYTES + (t % SPS) * BK * St::ROW_BYTES;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -354,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
 
     // ---- prologue -------------------------------------------------------------------
     __syncthreads();  // the previous tile's readers are done with every buffer
-    const int pro = min(PD, n_kv - 1);
+    const int pro = min(PD, n_stage - 1);
     for (int s = 0; s <= pro; ++s) issue_stage(s);
     stage_ready(0, pro);
 
@@ -365,39 +380,42 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     rowmax(s_cur, mx);
 
     // ---- main sweep ----------------------------------------------------------------------
-    // Fast path: steps whose successor needs no mask and whose prefetch stage lies fully
-    // below kv_end. Unrolled by the ring depth so every LDS slot is a compile-time offset
-    // and the two score tiles alternate without copies; constant vmcnt; no clamping.
-    static_assert(NBUF == 4, "the fast path is unrolled by a ring of 4 stages");
+    // Fast path: steps whose successor needs no mask and whose prefetched stage lies fully
+    // below kv_end. Unrolled over whole ring cycles so every LDS slot is a compile-time
+    // offset and the two score tiles alternate without copies; constant vmcnt; no clamping.
     constexpr int VM_STEADY = St::LPW * (PD - 1);
-    const int32_t n_full = kv_end / BK;  // stages with every key below kv_end
-    const int t_fast = min(t_mask - 1, n_full - 1 - PD);
+    static_assert(VM_STEADY < 16, "vmcnt immediate");
+    constexpr int GROUP = (NBUF * SPS) % 2 == 0 ? NBUF * SPS : 2 * NBUF * SPS;  // steps per unrolled group
+    const int32_t n_full = kv_end / St::BKS;  // stages with every key below kv_end
+    const int t_fast = min(t_mask - 1, (n_full - PD) * SPS - 1);
     tsp_f32x16 s_alt[RB];
-    auto fast_step = [&](auto u_const, int t, tsp_f32x16(&sc)[RB], tsp_f32x16(&sn)[RB]) {
-      constexpr int U = decltype(u_const)::value;  // t % 4
+    auto fast_step = [&](auto u_const, int t0) {
+      constexpr int U = decltype(u_const)::value;  // step t = t0 + U, t0 a multiple of GROUP
+      tsp_f32x16(&sc)[RB] = (U % 2 == 0) ? s_cur : s_alt;
+      tsp_f32x16(&sn)[RB] = (U % 2 == 0) ? s_alt : s_cur;
       if (rescale_needed(mx)) rescale(mx);
-      __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // stage t+1 landed (this wave's part)
-      __syncthreads();                                 // ... for every wave; slot (t-1)%4 free
-      {
-        const int64_t adv = (int64_t)(t + 1 + PD) * stage_stride;
-        const uint32_t base = smem_addr + ((U + 1 + PD) % NBUF) * St::STAGE_BYTES;
+      if constexpr ((U + 1) % SPS == 0) {  // step t+1 opens a new stage
+        __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // that stage landed (this wave's part)
+        __syncthreads();  // ... for every wave; the slot two stages back is free again
+        constexpr int NEXT = (U + 1) / SPS;  // stage of step t+1, relative to t0 / SPS
+        const int64_t adv = (int64_t)(t0 / SPS + NEXT + PD) * stage_stride;
+        const uint32_t base = smem_addr + ((NEXT + PD) % NBUF) * St::STAGE_BYTES;
 #pragma unroll
-        for (int q = 0; q < St::LPW; ++q) tsp_lds_dma16(dma_src[q] + adv, base + dma_slot[q]);
+        for (int q = 0; q < St::LPW; ++q)
+          tsp_lds_dma16((dma_isv[q] ? vbase : kbase) + adv, dma_voff[q], base + dma_slot[q]);
       }
       tsp_bf16x8 pf[RB][2];
-      qk((U + 1) % NBUF, sn);  // matrix pipe: next step's scores
-      softmax(sc, pf);         // vector pipe: this step's weights
-      pv(U % NBUF, pf);        // matrix pipe: this step's output
-      rowmax(sn, mx);          // vector pipe: next step's row max
+      qk(U + 1, sn);     // matrix pipe: next step's scores
+      softmax(sc, pf);   // vector pipe: this step's weights
+      pv(U, pf);         // matrix pipe: this step's output
+      rowmax(sn, mx);    // vector pipe: next step's row max
+    };
+    auto fast_group = [&]<int... Us>(std::integer_sequence<int, Us...>, int t0) {
+      (fast_step(std::integral_constant<int, Us>{}, t0), ...);
     };
     int t = 0;
-    for (; t + 4 <= t_fast; t += 4) {
-      fast_step(std::integral_constant<int, 0>{}, t + 0, s_cur, s_alt);
-      fast_step(std::integral_constant<int, 1>{}, t + 1, s_alt, s_cur);
-      fast_step(std::integral_constant<int, 2>{}, t + 2, s_cur, s_alt);
-      fast_step(std::integral_constant<int, 3>{}, t + 3, s_alt, s_cur);
-    }
-    int issued = t > 0 ? t + PD : pro;  // last stage issued so far
+    for (; t + GROUP <= t_fast; t += GROUP) fast_group(std::make_integer_sequence<int, GROUP>{}, t);
+    int issued = t > 0 ? t / SPS + PD : pro;  // last stage issued so far
 
     // General path: the masked steps near the diagonal, the partial last stage and the
     // ring drain.
@@ -405,8 +423,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       if (rescale_needed(mx)) rescale(mx);
       tsp_bf16x8 pf[RB][2];
       if (t + 1 < n_kv) {
-        stage_ready(t + 1, issued);
-        if (issued + 1 < n_kv) issue_stage(++issued);
+        if ((t + 1) % SPS == 0) {
+          stage_ready((t + 1) / SPS, issued);
+          if (issued + 1 < n_stage) issue_stage(++issued);
+        }
         qk(t + 1, s_alt);
         softmax(s_cur, pf);
         pv(t, pf);

@@ -36,19 +36,22 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 #ifndef TSP_DH128_NBUF
 #define TSP_DH128_NBUF 4
 #endif
+#ifndef TSP_DH128_SPS
+#define TSP_DH128_SPS 2
+#endif
 template <int DH>
 struct Bf16Cfg;
 template <>
 struct Bf16Cfg<64> {
-  static constexpr int NW = 4, RB = 2, NBUF = 4, OCC = 1;
+  static constexpr int NW = 4, RB = 2, NBUF = 4, SPS = 1, OCC = 1;
 };
 template <>
 struct Bf16Cfg<128> {
-  static constexpr int NW = TSP_DH128_NW, RB = 1, NBUF = TSP_DH128_NBUF, OCC = 2;
+  static constexpr int NW = TSP_DH128_NW, RB = 1, NBUF = TSP_DH128_NBUF, SPS = TSP_DH128_SPS, OCC = 2;
 };
 template <>
 struct Bf16Cfg<256> {
-  static constexpr int NW = 4, RB = 1, NBUF = 4, OCC = 1;
+  static constexpr int NW = 4, RB = 1, NBUF = 4, SPS = 1, OCC = 1;
 };
 
 // Tile configuration of one (dtype, dh) kernel.
@@ -60,7 +63,8 @@ struct KernelShape {
 
 template <int DH>
 KernelShape bf16_shape() {
-  return KernelShape{tsp::Bf16Stage<DH, Bf16Cfg<DH>::NW, Bf16Cfg<DH>::NBUF>::BK, Bf16Cfg<DH>::NW, Bf16Cfg<DH>::RB};
+  using C = Bf16Cfg<DH>;
+  return KernelShape{tsp::Bf16Stage<DH, C::NW, C::NBUF, C::SPS>::BK, C::NW, C::RB};
 }
 
 bool kernel_shape(int dtype, int64_t dh, KernelShape* ks) {
@@ -100,6 +104,8 @@ int plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_
   if (dtype != TSP_BF16 && dtype != TSP_F32) return fail(TSP_EUNSUPPORTED, "unknown dtype %d", dtype);
   if (!kernel_shape(dtype, dh, ks)) return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
   if (Hq > 65536 || B > 65536) return fail(TSP_EINVAL, "B or Hq too large");
+  // per-lane 32-bit byte offsets span one K/V stage: 64 keys of Hkv*dh elements
+  if (Hkv * dh > (int64_t(1) << 22)) return fail(TSP_EINVAL, "Hkv * dh above 2^22");
 
   const int64_t C = S_total / (2 * D);
   const int64_t grp = Hq / Hkv;
@@ -136,7 +142,8 @@ int plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_
 template <int DH>
 void launch_bf16(const TspParams& p, hipStream_t stream) {
   using C = Bf16Cfg<DH>;
-  hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::OCC>), dim3(p.n_units), dim3(C::NW * 64),
+  hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::SPS, C::OCC>), dim3(p.n_units),
+                     dim3(C::NW * 64),
                      0, stream, p);
 }
 
