@@ -40,6 +40,13 @@
 
 #include "attn_common.h"
 
+#ifndef TSP_SETPRIO
+#define TSP_SETPRIO 0
+#endif
+#ifndef TSP_SCHED
+#define TSP_SCHED 0
+#endif
+
 namespace tsp {
 
 typedef __bf16 tsp_bf16x4 __attribute__((ext_vector_type(4)));
@@ -405,10 +412,47 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
           tsp_lds_dma16((dma_isv[q] ? vbase : kbase) + adv, dma_voff[q], base + dma_slot[q]);
       }
       tsp_bf16x8 pf[RB][2];
+#if TSP_SETPRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
       qk(U + 1, sn);     // matrix pipe: next step's scores
+#if TSP_SETPRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
       softmax(sc, pf);   // vector pipe: this step's weights
+#if TSP_SETPRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
       pv(U, pf);         // matrix pipe: this step's output
+#if TSP_SETPRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
       rowmax(sn, mx);    // vector pipe: next step's row max
+#if TSP_SCHED == 1
+      // issue order: all operand reads, then QK MFMAs each followed by a slice of the
+      // softmax, then PV MFMAs each followed by a slice of the row max
+      __builtin_amdgcn_sched_group_barrier(0x100, NKK, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2 * NDB, 0);
+      for (int i = 0; i < NKK * RB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      for (int i = 0; i < 2 * NDB * RB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+#elif TSP_SCHED == 2
+      for (int i = 0; i < NKK * RB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      for (int i = 0; i < 2 * NDB * RB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+#endif
     };
     auto fast_group = [&]<int... Us>(std::integer_sequence<int, Us...>, int t0) {
       (fast_step(std::integral_constant<int, Us>{}, t0), ...);

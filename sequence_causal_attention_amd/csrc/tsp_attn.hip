@@ -39,6 +39,12 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 #ifndef TSP_DH128_SPS
 #define TSP_DH128_SPS 2
 #endif
+#ifndef TSP_DH128_RB
+#define TSP_DH128_RB 1
+#endif
+#ifndef TSP_DH128_OCC
+#define TSP_DH128_OCC 2
+#endif
 template <int DH>
 struct Bf16Cfg;
 template <>
@@ -47,7 +53,8 @@ struct Bf16Cfg<64> {
 };
 template <>
 struct Bf16Cfg<128> {
-  static constexpr int NW = TSP_DH128_NW, RB = 1, NBUF = TSP_DH128_NBUF, SPS = TSP_DH128_SPS, OCC = 2;
+  static constexpr int NW = TSP_DH128_NW, RB = TSP_DH128_RB, NBUF = TSP_DH128_NBUF, SPS = TSP_DH128_SPS,
+                       OCC = TSP_DH128_OCC;
 };
 template <>
 struct Bf16Cfg<256> {
