@@ -46,6 +46,9 @@
 #ifndef TSP_SCHED
 #define TSP_SCHED 0
 #endif
+#ifndef TSP_QK_SPLIT
+#define TSP_QK_SPLIT 0
+#endif
 
 namespace tsp {
 
@@ -287,11 +290,29 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
         kf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(kt + koff[kk]));
+#if TSP_QK_SPLIT
+      // two independent accumulation chains (even / odd reduction steps), summed at the end
+      tsp_f32x16 s2[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s2[rb][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; kk += 2)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[rb][kk], sc[rb], 0, 0, 0);
+          s2[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk + 1], qf[rb][kk + 1], s2[rb], 0, 0, 0);
+        }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sc[rb] += s2[rb];
+#else
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[rb][kk], sc[rb], 0, 0, 0);
+#endif
     };
     // key s*BK + 8(e/4) + 4*half + (e%4) of query column `col` is visible iff <= qpos
     auto mask = [&](int s, tsp_f32x16(&sc)[RB]) {

@@ -34,7 +34,7 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 #define TSP_DH128_NW 8
 #endif
 #ifndef TSP_DH128_NBUF
-#define TSP_DH128_NBUF 4
+#define TSP_DH128_NBUF 5
 #endif
 #ifndef TSP_DH128_SPS
 #define TSP_DH128_SPS 2
