@@ -3,8 +3,10 @@
 from .attention import (  # noqa: F401
     causal_attention,
     causal_attention_bruteforce,
+    causal_attention_range,
     causal_flops,
     kv_head_of,
+    merge_partials,
     softmax_scale,
     unmasked_pairs,
     visible,

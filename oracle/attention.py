@@ -145,27 +145,32 @@ def causal_attention(q, k, v, D: int, rank: int, rows=None, heads=None, block: i
     return out, lse
 
 
-def causal_attention_bruteforce(q, k, v, D: int, rank: int):
-    """Same definition as ``causal_attention`` as plain scalar loops (tiny inputs only)."""
+def causal_attention_bruteforce(q, k, v, D: int, rank: int, kv_begin: int = 0, kv_end=None):
+    """Same definition as ``causal_attention`` (keys restricted to [kv_begin, kv_end)) as
+    plain scalar loops (tiny inputs only). A row without a visible key gets out = 0 and
+    lse = -inf."""
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     B, S_local, Hq, dh = q.shape
     S_total, Hkv = k.shape[1], k.shape[2]
     pos = zigzag_positions(S_total, D, rank)
     scale = softmax_scale(dh)
+    kv_end = S_total if kv_end is None else kv_end
     out = np.zeros((B, S_local, Hq, dh))
-    lse = np.zeros((B, Hq, S_local))
+    lse = np.full((B, Hq, S_local), -np.inf)
     for b in range(B):
         for h in range(Hq):
             hk = kv_head_of(h, Hq, Hkv)
             for i in range(S_local):
                 p = int(pos[i])
                 scores = []
-                for j in range(S_total):
+                for j in range(kv_begin, kv_end):
                     if visible(np.array([j]), np.array([p]))[0, 0]:
                         dot = 0.0
                         for d in range(dh):
                             dot += q[b, i, h, d] * k[b, j, hk, d]
                         scores.append((j, scale * dot))
+                if not scores:
+                    continue
                 m = max(s for _, s in scores)
                 weights = [(j, math.exp(s - m)) for j, s in scores]
                 l = sum(w for _, w in weights)
@@ -192,3 +197,75 @@ def unmasked_pairs(S_total: int, D: int, rank: int) -> int:
 def causal_flops(B: int, Hq: int, dh: int, S_total: int, D: int, rank: int) -> int:
     """Algorithmic FLOPs: two products of 2*dh FLOP per visible pair per query head."""
     return 4 * B * Hq * dh * unmasked_pairs(S_total, D, rank)
+
+
+# --------------------------------------------------------------------------------------
+# Attention over a key range, and the merge of partial results.
+# "Folding Tensor and Sequence Parallelism ...", section 2 (Methodology): the K/V
+# all-gather is overlapped with computation (section 3, item 3: communication hidden
+# behind compute). Reading: a rank may attend to each gathered chunk of keys as it
+# arrives and combine the partial results. Each partial is the same definition with the
+# keys restricted to [kv_begin, kv_end); a row with no visible key in the range has the
+# empty sum: out = 0 and lse = -inf. Merging two partials over disjoint key sets is the
+# log-sum-exp combination of their softmax denominators, which reproduces the attention
+# over the union of the keys exactly.
+# --------------------------------------------------------------------------------------
+def causal_attention_range(q, k, v, D: int, rank: int, kv_begin: int, kv_end: int, rows=None, block: int = 256):
+    """Oracle forward restricted to keys j in [kv_begin, kv_end) (and j <= position)."""
+    q = _as_f64(q)
+    B, S_local, Hq, dh = q.shape
+    S_total, Hkv = k.shape[1], k.shape[2]
+    if not (0 <= kv_begin <= kv_end <= S_total):
+        raise ValueError("need 0 <= kv_begin <= kv_end <= S_total")
+    pos_all = zigzag_positions(S_total, D, rank)
+    rows = np.arange(S_local) if rows is None else np.asarray(rows, dtype=np.int64)
+    scale = softmax_scale(dh)
+    out = np.zeros((B, len(rows), Hq, dh))
+    lse = np.full((B, Hq, len(rows)), -np.inf)
+    for b in range(B):
+        kv_cache = {}
+        for h in range(Hq):
+            hk = kv_head_of(h, Hq, Hkv)
+            if hk not in kv_cache:
+                kv_cache = {hk: (_as_f64(k[b, :, hk, :]), _as_f64(v[b, :, hk, :]))}
+            kb, vb = kv_cache[hk]
+            for start in range(0, len(rows), block):
+                r = rows[start:start + block]
+                p = pos_all[r]
+                hi = min(kv_end, int(p.max()) + 1)
+                if hi <= kv_begin:
+                    continue  # no row of the block sees a key of the range
+                keys = np.arange(kv_begin, hi, dtype=np.int64)
+                s = scale * (q[b, r, h, :] @ kb[kv_begin:hi].T)
+                vis = visible(keys, p)
+                s = np.where(vis, s, -np.inf)
+                any_vis = vis.any(axis=1)
+                m = np.where(any_vis, s.max(axis=1), 0.0)[:, None]
+                w = np.where(vis, np.exp(s - m), 0.0)
+                l = w.sum(axis=1, keepdims=True)
+                o = np.where(any_vis[:, None], (w @ vb[kv_begin:hi]) / np.where(l > 0, l, 1.0), 0.0)
+                out[b, start:start + len(r), h, :] = o
+                lse[b, h, start:start + len(r)] = np.where(any_vis, (m + np.log(np.where(l > 0, l, 1.0)))[:, 0], -np.inf)
+    return out, lse
+
+
+def merge_partials(out_a, lse_a, out_b, lse_b):
+    """Combine two partial results over disjoint key sets (log-sum-exp weights).
+
+    out: [B, rows, Hq, dh]; lse: [B, Hq, rows]. A partial with lse = -inf contributes
+    nothing; if both are empty the result is out = 0, lse = -inf.
+    """
+    out_a, out_b = _as_f64(out_a), _as_f64(out_b)
+    lse_a, lse_b = _as_f64(lse_a), _as_f64(lse_b)
+    m = np.maximum(lse_a, lse_b)
+    finite = np.isfinite(m)
+    m0 = np.where(finite, m, 0.0)
+    wa = np.where(np.isfinite(lse_a), np.exp(lse_a - m0), 0.0)
+    wb = np.where(np.isfinite(lse_b), np.exp(lse_b - m0), 0.0)
+    tot = wa + wb
+    lse = np.where(finite, m0 + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    ta = np.where(tot > 0, wa / np.where(tot > 0, tot, 1.0), 0.0)
+    tb = np.where(tot > 0, wb / np.where(tot > 0, tot, 1.0), 0.0)
+    # weights are [B, Hq, rows]; outputs are [B, rows, Hq, dh]
+    out = out_a * ta.transpose(0, 2, 1)[..., None] + out_b * tb.transpose(0, 2, 1)[..., None]
+    return out, lse

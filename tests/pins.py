@@ -2,7 +2,7 @@
 
 Each ``pin_*`` takes an oracle namespace ``o`` (attributes ``causal_attention``,
 ``causal_attention_bruteforce``, ``zigzag_positions``, ``unmasked_pairs``,
-``kv_head_of``) and raises AssertionError when the implementation breaks the pin. The
+``kv_head_of``, ``causal_attention_range``, ``merge_partials``) and raises AssertionError when the implementation breaks the pin. The
 same pins run against deliberately broken copies in test_oracle_mutants.py, which
 shows that a plausible mistake anywhere in the oracle trips at least one of them.
 """
@@ -226,6 +226,61 @@ def pin_shift_invariance(o):
     assert np.allclose(lse1 - lse0, shift, rtol=0, atol=1e-12)
 
 
+# -- attention over key ranges and the merge of partials -------------------------------
+
+def pin_range_bruteforce(o):
+    """Key-range partials == scalar loops restricted to the range (incl. empty rows)."""
+    for n, case in enumerate(TINY):
+        q, k, v = _tiny_inputs(case, 90 + n)
+        S, D, r = case[1], case[2], case[3]
+        for lo, hi in [(0, S), (0, S // 3), (S // 3, S), (S // 4, S // 2 + 1), (S - 1, S), (5, 5)]:
+            out_b, lse_b = o.causal_attention_range(q, k, v, D, r, lo, hi, block=3)
+            out_r, lse_r = o.causal_attention_bruteforce(q, k, v, D, r, lo, hi)
+            assert np.allclose(out_b, out_r, rtol=0, atol=1e-12), (case, lo, hi)
+            assert np.array_equal(np.isinf(lse_b), np.isinf(lse_r)), (case, lo, hi)
+            fin = np.isfinite(lse_r)
+            assert np.allclose(lse_b[fin], lse_r[fin], rtol=0, atol=1e-12), (case, lo, hi)
+
+
+def pin_range_partition(o):
+    """Merging the partials of any split of [0, S_total) reproduces the full attention
+    (the softmax denominator is a sum over keys, split by the log-sum-exp combination)."""
+    for n, (B, S, D, r, Hq, Hkv, dh) in enumerate([(1, 32, 4, 1, 2, 1, 8), (2, 48, 3, 2, 4, 2, 4),
+                                                    (1, 64, 1, 0, 2, 2, 8)]):
+        q, k, v = _tiny_inputs((B, S, D, r, Hq, Hkv, dh), 100 + n)
+        full_out, full_lse = o.causal_attention(q, k, v, D, r)
+        C = S // (2 * D)
+        cuts_list = [list(range(0, S + 1, C)),          # the all-gather's chunks
+                     [0, 3, 3, 17, S - 2, S],           # ragged, with an empty range
+                     [0, S]]
+        for cuts in cuts_list:
+            parts = [o.causal_attention_range(q, k, v, D, r, a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+            for order in (parts, parts[::-1]):
+                acc_o, acc_l = order[0]
+                for po, pl in order[1:]:
+                    acc_o, acc_l = o.merge_partials(acc_o, acc_l, po, pl)
+                assert np.allclose(acc_o, full_out, rtol=0, atol=1e-12), (S, D, cuts)
+                assert np.allclose(acc_l, full_lse, rtol=0, atol=1e-12), (S, D, cuts)
+
+
+def pin_merge_identity(o):
+    """An empty partial (lse = -inf) is the identity of the merge; the merge commutes."""
+    rng = np.random.default_rng(110)
+    out_a = rng.standard_normal((1, 5, 2, 4))
+    lse_a = rng.standard_normal((1, 2, 5))
+    out_e = np.zeros_like(out_a)
+    lse_e = np.full_like(lse_a, -np.inf)
+    mo, ml = o.merge_partials(out_a, lse_a, out_e, lse_e)
+    assert np.array_equal(mo, out_a) and np.array_equal(ml, lse_a)
+    mo, ml = o.merge_partials(out_e, lse_e, out_e, lse_e)
+    assert np.all(mo == 0) and np.all(np.isneginf(ml))
+    out_b = rng.standard_normal((1, 5, 2, 4))
+    lse_b = rng.standard_normal((1, 2, 5))
+    m1 = o.merge_partials(out_a, lse_a, out_b, lse_b)
+    m2 = o.merge_partials(out_b, lse_b, out_a, lse_a)
+    assert np.allclose(m1[0], m2[0], rtol=0, atol=1e-15) and np.allclose(m1[1], m2[1], rtol=0, atol=1e-15)
+
+
 ALL_PINS = [
     pin_zigzag_golden,
     pin_zigzag_permutation,
@@ -240,4 +295,7 @@ ALL_PINS = [
     pin_first_position,
     pin_gqa_equivalence,
     pin_shift_invariance,
+    pin_range_bruteforce,
+    pin_range_partition,
+    pin_merge_identity,
 ]

@@ -84,7 +84,7 @@ WRAPS = {
 def _namespace():
     ns = types.SimpleNamespace()
     for n in ("causal_attention", "causal_attention_bruteforce", "zigzag_positions",
-              "unmasked_pairs", "kv_head_of"):
+              "unmasked_pairs", "kv_head_of", "causal_attention_range", "merge_partials"):
         setattr(ns, n, getattr(A, n))
     return ns
 
@@ -116,6 +116,34 @@ def test_wrapped_mutant_is_caught(name):
     with np.errstate(all="ignore"):
         failed = _failures(ns)
     assert failed, f"mutant {name} passed every pin"
+
+
+def _merge_linear(out_a, lse_a, out_b, lse_b):
+    # plausible mistake: weights from exp(lse) without the shared max, and lse summed
+    wa, wb = np.exp(lse_a), np.exp(lse_b)
+    t = (wa + wb).transpose(0, 2, 1)[..., None]
+    return (out_a * wa.transpose(0, 2, 1)[..., None] + out_b * wb.transpose(0, 2, 1)[..., None]) / t, lse_a + lse_b
+
+
+def _range_inclusive_end(f):
+    def g(q, k, v, D, rank, kv_begin, kv_end, rows=None, block=256):
+        return f(q, k, v, D, rank, kv_begin, min(kv_end + 1, k.shape[1]), rows=rows, block=block)
+    return g
+
+
+def test_merge_mistake_is_caught():
+    ns = _namespace()
+    ns.merge_partials = _merge_linear
+    with np.errstate(all="ignore"):
+        assert "pin_range_partition" in _failures(ns)
+
+
+def test_range_end_mistake_is_caught():
+    ns = _namespace()
+    ns.causal_attention_range = _range_inclusive_end(A.causal_attention_range)
+    with np.errstate(all="ignore"):
+        failed = _failures(ns)
+    assert "pin_range_bruteforce" in failed or "pin_range_partition" in failed
 
 
 def test_blocked_form_error_is_caught():
