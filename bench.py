@@ -98,6 +98,9 @@ def main():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-pipeline", action="store_true",
+                    help="time the chunk-pipelined form instead: one key-range launch per gathered "
+                         "chunk (2D of them, in ring arrival order) merged into the running result")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run plain device copies of MIB MiB (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -135,8 +138,19 @@ def main():
     stream = torch.cuda.Stream(dev)  # default priority
     torch.cuda.synchronize()
 
+    # ring arrival order of the 2D gathered chunks: the rank's own pair first
+    chunks = sorted(range(2 * w.D), key=lambda c: ((c % w.D - rank) % w.D, c))
+    bounds = [(c * w.C, (c + 1) * w.C) for c in chunks]
+    part_o, part_l = torch.empty_like(out), torch.empty_like(lse)
+
     def step():
-        tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream)
+        if not args.chunk_pipeline:
+            tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream)
+            return
+        tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream, kv_range=bounds[0])
+        for rng in bounds[1:]:
+            tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=part_o, lse=part_l, stream=stream, kv_range=rng)
+            tsp.merge(out, lse, part_o, part_l, out=out, lse=lse, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -161,7 +175,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.chunk_pipeline:
         cpu = cpu_baseline(w, rank, q, k, v, args.cpu_budget)
 
     line = {
@@ -182,6 +196,8 @@ def main():
             "workload": w.name, "B": w.B, "S_total": w.S_total, "D": w.D, "rank": rank, "Hq": w.Hq,
             "Hkv": w.Hkv, "dh": w.dh, "local_queries": w.S_local, "flops_per_step": flops,
             "parallelism": "one sequence-parallel rank's shard on 1 GPU",
+            "form": (f"chunk pipeline: {len(bounds)} key-range launches + {len(bounds) - 1} merges"
+                     if args.chunk_pipeline else "single launch"),
         },
         "roofline": {
             "bound": "mfma",
@@ -189,7 +205,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(w.name, flops),
+            "traffic": None if args.chunk_pipeline else measured_traffic(w.name, flops),
             "kernel_ms": round(kernel_ms, 4),
         },
         "cpu_baseline": cpu,

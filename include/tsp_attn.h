@@ -80,6 +80,37 @@ int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, vo
                  int64_t Hkv, int64_t dh, int dtype, void* stream);
 
 /*
+ * tsp_attn_fwd_range -- tsp_attn_fwd restricted to the keys j in [kv_begin, kv_end)
+ * (0 <= kv_begin <= kv_end <= S_total), still causal by global position. A local row
+ * with no visible key in the range gets out = 0 and lse = -inf. Partials over disjoint
+ * ranges combine exactly with tsp_attn_merge, so a rank can attend to each gathered
+ * chunk of K/V as it arrives ("Folding Tensor and Sequence Parallelism ...", section 2,
+ * attention layers: the all-gather along the sequence; section 3 item 3: communication
+ * overlapped with compute). Only keys in [kv_begin rounded down to 64, kv_end) and below
+ * the rank's last position are read. Same arguments, layouts, ownership and errors as
+ * tsp_attn_fwd, plus TSP_EINVAL for a range outside [0, S_total].
+ */
+int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_full, void* out,
+                       float* lse, int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq,
+                       int64_t Hkv, int64_t dh, int64_t kv_begin, int64_t kv_end, int dtype,
+                       void* stream);
+
+/*
+ * tsp_attn_merge -- combine two partial results over disjoint key sets:
+ *   lse = log(exp(lse_a) + exp(lse_b)),
+ *   out = exp(lse_a - lse) * out_a + exp(lse_b - lse) * out_b,
+ * a partial with lse = -inf contributing nothing (both -inf: out = 0, lse = -inf).
+ *   out_a, out_b, out   device, [B, S_local, Hq, dh] contiguous, element type `dtype`
+ *   lse_a, lse_b, lse   device, [B, Hq, S_local] float32
+ * out / lse may be the same buffers as out_a / lse_a (in-place accumulation); no other
+ * overlap is allowed. Pointers 16-byte aligned, dh in {64, 128, 256}. Enqueued on
+ * `stream`. Returns TSP_OK, TSP_EINVAL, TSP_EUNSUPPORTED or TSP_ELAUNCH.
+ */
+int tsp_attn_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b,
+                   void* out, float* lse, int64_t B, int64_t S_local, int64_t Hq, int64_t dh,
+                   int dtype, void* stream);
+
+/*
  * tsp_attn_zigzag_positions -- the zigzag map on the host: writes g(i) for the 2C local
  * rows of `rank` into out_host (caller-owned host memory of 2C int64).
  * ("Folding Tensor and Sequence Parallelism ...", section 2, zigzag partitioning.)

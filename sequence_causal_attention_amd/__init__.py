@@ -37,6 +37,9 @@ _VP = ctypes.c_void_p
 SIGNATURES = {
     "tsp_attn_fwd": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                     ctypes.c_int, _VP]),
+    "tsp_attn_fwd_range": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                          _I64, _I64, ctypes.c_int, _VP]),
+    "tsp_attn_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "tsp_attn_zigzag_positions": (ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(_I64)]),
     "tsp_attn_zigzag_positions_device": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP]),
     "tsp_attn_unmasked_pairs": (_I64, [_I64, _I64, _I64]),
@@ -87,12 +90,14 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D: int, rank: int,
-        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None, kv_range=None):
     """Causal attention of this rank's zigzag queries against the full K/V.
 
     q_local [B, 2C, Hq, dh], k_full / v_full [B, S_total, Hkv, dh]: contiguous, same
     device and dtype (bf16 or fp32). Returns (out [B, 2C, Hq, dh] same dtype,
     lse [B, Hq, 2C] fp32). ``out`` / ``lse`` may be passed in preallocated.
+    ``kv_range=(begin, end)`` restricts the keys (tsp_attn_fwd_range): rows without a
+    visible key in the range get out = 0, lse = -inf.
     The call is asynchronous on ``stream`` (default: the current stream).
     """
     for name, t in (("q_local", q_local), ("k_full", k_full), ("v_full", v_full)):
@@ -124,9 +129,37 @@ def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D:
     if stream is None:
         stream = torch.cuda.current_stream(q_local.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lo, hi = (0, S_total) if kv_range is None else (int(kv_range[0]), int(kv_range[1]))
     with torch.cuda.device(q_local.device):
-        st = lib().tsp_attn_fwd(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
-                                lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, code, handle)
+        st = lib().tsp_attn_fwd_range(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, lo, hi, code, handle)
+    _check(st)
+    return out, lse
+
+
+def merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor, lse_b: torch.Tensor, *,
+          out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+    """Log-sum-exp merge of two partials (tsp_attn_merge). out/lse default to new
+    tensors; pass out=out_a, lse=lse_a to accumulate in place."""
+    for t in (out_a, lse_a, out_b, lse_b):
+        if not t.is_cuda or not t.is_contiguous():
+            raise TspAttnError(TSP_EINVAL, "merge operands must be contiguous GPU tensors")
+    if out_a.shape != out_b.shape or out_a.dtype != out_b.dtype or out_a.dim() != 4:
+        raise TspAttnError(TSP_EINVAL, "out_a / out_b must match, [B, S_local, Hq, dh]")
+    B, S_local, Hq, dh = out_a.shape
+    if tuple(lse_a.shape) != (B, Hq, S_local) or lse_b.shape != lse_a.shape or lse_a.dtype != torch.float32:
+        raise TspAttnError(TSP_EINVAL, "lse_a / lse_b must be float32 [B, Hq, S_local]")
+    code = _dtype_code(out_a)
+    out = torch.empty_like(out_a) if out is None else out
+    lse = torch.empty_like(lse_a) if lse is None else lse
+    if out.shape != out_a.shape or out.dtype != out_a.dtype or lse.shape != lse_a.shape:
+        raise TspAttnError(TSP_EINVAL, "out / lse must match the operands")
+    if stream is None:
+        stream = torch.cuda.current_stream(out_a.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(out_a.device):
+        st = lib().tsp_attn_merge(out_a.data_ptr(), lse_a.data_ptr(), out_b.data_ptr(), lse_b.data_ptr(),
+                                  out.data_ptr(), lse.data_ptr(), B, S_local, Hq, dh, code, handle)
     _check(st)
     return out, lse
 

@@ -32,6 +32,7 @@ struct TspParams {
   int32_t n_pairs;       // ceil(n_qtiles / 2): mirrored tile pairs per (b, head group)
   int32_t n_hgroups;     // grp / GH
   int32_t n_units;       // B * Hkv * n_hgroups * n_pairs workgroups
+  int32_t kv_lo, kv_hi;  // only keys in [kv_lo, kv_hi) take part (whole sequence: 0, S_total)
   float scale_log2;      // log2(e) / sqrt(dh): scores go straight to the exp2 domain
 };
 

@@ -158,8 +158,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
   const int32_t b = unit / p.Hkv;
 
   const int64_t kv_row_stride = (int64_t)p.Hkv * DH;  // elements between consecutive keys
-  const uint16_t* __restrict__ kbase = kg + ((int64_t)b * p.S_total * p.Hkv + hk) * DH;
-  const uint16_t* __restrict__ vbase = vg + ((int64_t)b * p.S_total * p.Hkv + hk) * DH;
+  // The sweep starts at the stage boundary at or below kv_lo; key indices below are
+  // relative to it (keys in [kv_base, kv_lo) are loaded but masked).
+  const int32_t kv_base = (p.kv_lo / St::BKS) * St::BKS;
+  const int32_t kv_lo_rel = p.kv_lo - kv_base;
+  const uint16_t* __restrict__ kbase = kg + (((int64_t)b * p.S_total + kv_base) * p.Hkv + hk) * DH;
+  const uint16_t* __restrict__ vbase = vg + (((int64_t)b * p.S_total + kv_base) * p.Hkv + hk) * DH;
   const int pos_blocks = p.BQ / 32;  // row blocks per head in a tile
 
   // ---- per-lane LDS read offsets (constant over the sweep) ------------------------------
@@ -214,7 +218,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     if (which == 1 && qt == p.n_qtiles - 1 - pair) break;  // middle tile of an odd count
     const int32_t row0 = qt * p.BQ;
     const int32_t last_row = min(row0 + p.BQ, p.S_local) - 1;
-    const int32_t kv_end = tsp_zigzag_position(last_row, p.C, p.D, p.rank) + 1;
+    // relative end of the keys this tile sweeps: its last position, or the range end
+    const int32_t kv_end = min(p.kv_hi, tsp_zigzag_position(last_row, p.C, p.D, p.rank) + 1) - kv_base;
     const int32_t n_kv = (kv_end + BK - 1) / BK;             // pipeline steps
     const int32_t n_stage = (kv_end + St::BKS - 1) / St::BKS;  // stages
 
@@ -230,12 +235,30 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       const int32_t r = row0 + pb * 32 + col;
       rvalid[rb] = r < p.S_local;
       lrow[rb] = min(r, p.S_local - 1);
-      qpos[rb] = tsp_zigzag_position(lrow[rb], p.C, p.D, p.rank);
+      // last visible key of the row: its position, or the range end if that comes first
+      qpos[rb] = min(tsp_zigzag_position(lrow[rb], p.C, p.D, p.rank), p.kv_hi - 1);
       wave_first = min(wave_first, row0 + pb * 32);
     }
     const int32_t wave_min_pos = tsp_zigzag_position(min(wave_first, p.S_local - 1), p.C, p.D, p.rank);
-    // steps [0, t_mask) are visible to every row of the wave; later steps are masked
-    const int32_t t_mask = min(n_kv, (wave_min_pos + 1) / BK);
+    // steps [u_left, t_mask) are visible to every row of the wave; earlier steps hold keys
+    // below kv_lo, later ones keys past some row's position or the range end: all masked
+    const int32_t t_mask = min(n_kv, max(0, min(wave_min_pos + 1, p.kv_hi) - kv_base) / BK);
+    const int32_t u_left = (kv_lo_rel + BK - 1) / BK;
+
+    if (kv_end <= kv_lo_rel) {  // no key of the range is visible to any row of the tile
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (rvalid[rb]) {
+          uint16_t* op = og + (((int64_t)b * p.S_local + lrow[rb]) * p.Hq + head[rb]) * DH + 4 * half;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) *reinterpret_cast<tsp_u32x2*>(op + db * 32 + 8 * a) = tsp_u32x2{0u, 0u};
+          if (half == 0) p.lse[((int64_t)b * p.Hq + head[rb]) * p.S_local + lrow[rb]] = -INFINITY;
+        }
+      }
+      continue;
+    }
 
     // ---- Q^T operands stay in registers ------------------------------------------------
     tsp_bf16x8 qf[RB][NKK];
@@ -314,16 +337,21 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
           sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[rb][kk], sc[rb], 0, 0, 0);
 #endif
     };
-    // key s*BK + 8(e/4) + 4*half + (e%4) of query column `col` is visible iff <= qpos
+    // key kv_base + s*BK + 8(e/4) + 4*half + (e%4) of query column `col` is visible iff
+    // it is <= qpos (the query's position, capped below kv_hi) and >= kv_lo
     auto mask = [&](int s, tsp_f32x16(&sc)[RB]) {
+      const int32_t lo = kv_lo_rel - s * BK - 4 * half;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int32_t lim = qpos[rb] - s * BK - 4 * half;
+        const int32_t hi = qpos[rb] - kv_base - s * BK - 4 * half;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if ((8 * (e >> 2) + (e & 3)) > lim) sc[rb][e] = -INFINITY;
+        for (int e = 0; e < 16; ++e) {
+          const int off = 8 * (e >> 2) + (e & 3);
+          if (off > hi || off < lo) sc[rb][e] = -INFINITY;
+        }
       }
     };
+    auto needs_mask = [&](int s) { return s >= t_mask || s < u_left; };
     auto rowmax = [&](const tsp_f32x16(&sc)[RB], float(&mx)[RB]) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -345,7 +373,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const float m_new = fmaxf(m_run[rb], mx[rb]);
-        const float alpha = tsp_exp2(m_run[rb] - m_new);
+        // a row with no visible key yet (both -inf) keeps its zero state
+        const float alpha = m_new == -INFINITY ? 1.f : tsp_exp2(m_run[rb] - m_new);
         m_run[rb] = m_new;
         l_run[rb] *= alpha;
 #pragma unroll
@@ -354,10 +383,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
           for (int e = 0; e < 16; ++e) acc[rb][db][e] *= alpha;
       }
     };
-    auto softmax = [&](const tsp_f32x16(&sc)[RB], tsp_bf16x8(&pf)[RB][2]) {
+    // guard: a row may not have seen a visible key yet (m_run = -inf), so use 0 as its
+    // exponent offset; its scores are all -inf and its weights 0
+    auto softmax = [&](const tsp_f32x16(&sc)[RB], tsp_bf16x8(&pf)[RB][2], bool guard) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float mneg = -m_run[rb];
+        const float mneg = (guard && m_run[rb] == -INFINITY) ? 0.f : -m_run[rb];
         float lsum = 0.f;
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -404,7 +435,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     tsp_f32x16 s_cur[RB];
     float mx[RB];
     qk(0, s_cur);
-    if (t_mask == 0) mask(0, s_cur);
+    if (needs_mask(0)) mask(0, s_cur);
     rowmax(s_cur, mx);
 
     // ---- main sweep ----------------------------------------------------------------------
@@ -415,7 +446,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     static_assert(VM_STEADY < 16, "vmcnt immediate");
     constexpr int GROUP = (NBUF * SPS) % 2 == 0 ? NBUF * SPS : 2 * NBUF * SPS;  // steps per unrolled group
     const int32_t n_full = kv_end / St::BKS;  // stages with every key below kv_end
-    const int t_fast = min(t_mask - 1, (n_full - PD) * SPS - 1);
+    const int t_fast = u_left == 0 ? min(t_mask - 1, (n_full - PD) * SPS - 1) : 0;
     tsp_f32x16 s_alt[RB];
     auto fast_step = [&](auto u_const, int t0) {
       constexpr int U = decltype(u_const)::value;  // step t = t0 + U, t0 a multiple of GROUP
@@ -440,7 +471,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
 #if TSP_SETPRIO
       __builtin_amdgcn_s_setprio(0);
 #endif
-      softmax(sc, pf);   // vector pipe: this step's weights
+      softmax(sc, pf, false);  // vector pipe: this step's weights
 #if TSP_SETPRIO
       __builtin_amdgcn_s_setprio(1);
 #endif
@@ -493,14 +524,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
           if (issued + 1 < n_stage) issue_stage(++issued);
         }
         qk(t + 1, s_alt);
-        softmax(s_cur, pf);
+        softmax(s_cur, pf, true);
         pv(t, pf);
-        if (t + 1 >= t_mask) mask(t + 1, s_alt);
+        if (needs_mask(t + 1)) mask(t + 1, s_alt);
         rowmax(s_alt, mx);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_alt[rb];
       } else {
-        softmax(s_cur, pf);
+        softmax(s_cur, pf, true);
         pv(t, pf);
       }
     }
@@ -509,7 +540,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float l = tsp_sum_halves(l_run[rb]);
-      const float inv = 1.0f / l;
+      const float inv = l > 0.f ? 1.0f / l : 0.f;  // l = 0: no visible key in the range
       if (rvalid[rb]) {
         uint16_t* op = og + (((int64_t)b * p.S_local + lrow[rb]) * p.Hq + head[rb]) * DH + 4 * half;
 #pragma unroll
@@ -523,7 +554,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
           }
         if (half == 0)
           p.lse[((int64_t)b * p.Hq + head[rb]) * p.S_local + lrow[rb]] =
-              (m_run[rb] + __builtin_amdgcn_logf(l)) * TSP_LN2;
+              l > 0.f ? (m_run[rb] + __builtin_amdgcn_logf(l)) * TSP_LN2 : -INFINITY;
       }
     }
   }

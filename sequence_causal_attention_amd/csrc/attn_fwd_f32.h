@@ -53,7 +53,9 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(TspParams p) {
     if (which == 1 && qt == p.n_qtiles - 1 - pair) break;
     const int32_t row0 = qt * p.BQ;
     const int32_t last_row = min(row0 + p.BQ, p.S_local) - 1;
-    const int32_t kv_end = tsp_zigzag_position(last_row, p.C, p.D, p.rank) + 1;
+    // keys [kv_lo, kv_end) take part: up to the tile's last position, or the range end
+    const int32_t kv_end = min(p.kv_hi, tsp_zigzag_position(last_row, p.C, p.D, p.rank) + 1);
+    const int32_t j0 = p.kv_lo / BK;  // first key tile of the range
     const int32_t n_kv = (kv_end + BK - 1) / BK;
 
     const int pb = wave % pos_blocks, hh = wave / pos_blocks;
@@ -62,7 +64,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(TspParams p) {
     const int32_t r = first + col;
     const bool rvalid = r < p.S_local;
     const int32_t lrow = min(r, p.S_local - 1);
-    const int32_t qpos = tsp_zigzag_position(lrow, p.C, p.D, p.rank);
+    // last visible key of the row: its position, or the range end if that comes first
+    const int32_t qpos = min(tsp_zigzag_position(lrow, p.C, p.D, p.rank), p.kv_hi - 1);
     const bool wave_active = first < p.S_local;
     const int32_t wave_min_pos = tsp_zigzag_position(min(first, p.S_local - 1), p.C, p.D, p.rank);
     const int32_t wave_max_pos = tsp_zigzag_position(min(first + 31, p.S_local - 1), p.C, p.D, p.rank);
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(TspParams p) {
       for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int j = 0; j < n_kv; ++j) {
+    for (int j = j0; j < n_kv; ++j) {
       const int32_t kv0 = j * BK;
       __syncthreads();  // previous tile fully consumed
 #pragma unroll
@@ -109,14 +112,17 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(TspParams p) {
       for (int kk = 0; kk < DH / 2; ++kk)
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(sk[col * KP + 2 * kk + half], qf[kk], s, 0, 0, 0);
 
-      // lane holds keys kv0 + 8(e/4) + 4*half + (e%4) of query column `col`
-      const bool need_mask = kv0 + BK - 1 > wave_min_pos;
-      const int32_t lim = qpos - kv0 - 4 * half;
+      // lane holds keys kv0 + 8(e/4) + 4*half + (e%4) of query column `col`: visible iff
+      // <= qpos and >= kv_lo
+      const bool need_mask = kv0 + BK - 1 > min(wave_min_pos, p.kv_hi - 1) || kv0 < p.kv_lo;
+      const int32_t hi = qpos - kv0 - 4 * half;
+      const int32_t lo = p.kv_lo - kv0 - 4 * half;
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float x = s[e];
-        if (need_mask && (8 * (e >> 2) + (e & 3)) > lim) x = -INFINITY;
+        const int off = 8 * (e >> 2) + (e & 3);
+        if (need_mask && (off > hi || off < lo)) x = -INFINITY;
         s[e] = x;
         mx = fmaxf(mx, x);
       }
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(TspParams p) {
       const float mt = mx * p.scale_log2;
       if (__builtin_amdgcn_ballot_w64(mt > m_run + TSP_RESCALE_SLACK) != 0) {
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = tsp_exp2(m_run - m_new);
+        const float alpha = m_new == -INFINITY ? 1.f : tsp_exp2(m_run - m_new);  // still no visible key
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
@@ -132,9 +138,10 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(TspParams p) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
       }
+      const float mneg = m_run == -INFINITY ? 0.f : -m_run;  // no visible key yet: weights 0
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        s[e] = tsp_exp2(fmaf(s[e], p.scale_log2, -m_run));
+        s[e] = tsp_exp2(fmaf(s[e], p.scale_log2, mneg));
         l_run += s[e];
       }
 
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(TspParams p) {
 
     if (wave_active) {
       const float l = tsp_sum_halves(l_run);
-      const float inv = 1.0f / l;
+      const float inv = l > 0.f ? 1.0f / l : 0.f;  // l = 0: no visible key in the range
       if (rvalid) {
         float* op = og + (((int64_t)b * p.S_local + lrow) * p.Hq + head) * DH + 4 * half;
 #pragma unroll
@@ -161,7 +168,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(TspParams p) {
                 make_float4(acc[db][4 * a] * inv, acc[db][4 * a + 1] * inv, acc[db][4 * a + 2] * inv,
                             acc[db][4 * a + 3] * inv);
         if (half == 0)
-          p.lse[((int64_t)b * p.Hq + head) * p.S_local + lrow] = (m_run + __builtin_amdgcn_logf(l)) * TSP_LN2;
+          p.lse[((int64_t)b * p.Hq + head) * p.S_local + lrow] =
+              l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * TSP_LN2 : -INFINITY;
       }
     }
     __syncthreads();

@@ -12,6 +12,7 @@
 #include "attn_common.h"
 #include "attn_fwd_bf16.h"
 #include "attn_fwd_f32.h"
+#include "attn_merge.h"
 
 namespace {
 
@@ -168,9 +169,9 @@ __global__ void zigzag_dump_kernel(int32_t* out, int32_t n, int32_t C, int32_t D
 
 extern "C" {
 
-int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse, int64_t B,
-                 int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
-                 void* stream) {
+int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse,
+                       int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh,
+                       int64_t kv_begin, int64_t kv_end, int dtype, void* stream) {
   if (!q_local || !k_full || !v_full || !out || !lse) return fail(TSP_EINVAL, "null pointer argument");
   if (!aligned16(q_local) || !aligned16(k_full) || !aligned16(v_full) || !aligned16(out) || !aligned16(lse))
     return fail(TSP_EINVAL, "pointers must be 16-byte aligned");
@@ -178,6 +179,11 @@ int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, vo
   KernelShape ks{};
   int st = plan(B, S_total, D, rank, Hq, Hkv, dh, dtype, &p, &ks);
   if (st != TSP_OK) return st;
+  if (kv_begin < 0 || kv_begin > kv_end || kv_end > S_total)
+    return fail(TSP_EINVAL, "key range [%lld, %lld) not inside [0, %lld]", (long long)kv_begin,
+                (long long)kv_end, (long long)S_total);
+  p.kv_lo = (int32_t)kv_begin;
+  p.kv_hi = (int32_t)kv_end;
   p.q = q_local;
   p.k = k_full;
   p.v = v_full;
@@ -200,6 +206,48 @@ int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, vo
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TSP_ELAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return TSP_OK;
+}
+
+int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse, int64_t B,
+                 int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
+                 void* stream) {
+  return tsp_attn_fwd_range(q_local, k_full, v_full, out, lse, B, S_total, D, rank, Hq, Hkv, dh, 0, S_total, dtype,
+                            stream);
+}
+
+int tsp_attn_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,
+                   float* lse, int64_t B, int64_t S_local, int64_t Hq, int64_t dh, int dtype, void* stream) {
+  if (!out_a || !lse_a || !out_b || !lse_b || !out || !lse) return fail(TSP_EINVAL, "null pointer argument");
+  if (!aligned16(out_a) || !aligned16(out_b) || !aligned16(out) || !aligned16(lse_a) || !aligned16(lse_b) ||
+      !aligned16(lse))
+    return fail(TSP_EINVAL, "pointers must be 16-byte aligned");
+  if (B < 1 || S_local < 1 || Hq < 1) return fail(TSP_EINVAL, "B, S_local and Hq must be >= 1");
+  if (S_local > 0x7fffffff || Hq > 65536 || B > 65536) return fail(TSP_EINVAL, "sizes too large");
+  if (dtype != TSP_BF16 && dtype != TSP_F32) return fail(TSP_EUNSUPPORTED, "unknown dtype %d", dtype);
+  if (dh != 64 && dh != 128 && dh != 256) return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
+  tsp::MergeParams mp{out_a, lse_a, out_b, lse_b, out, lse, B * S_local * Hq, (int32_t)S_local, (int32_t)Hq};
+  const int ept = dtype == TSP_BF16 ? 8 : 4;
+  const int64_t threads = mp.rows * (dh / ept);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (dtype == TSP_BF16) {
+    switch (dh) {
+      case 64: hipLaunchKernelGGL((tsp::attn_merge_kernel<uint16_t, 64>), grid, dim3(256), 0, st, mp); break;
+      case 128: hipLaunchKernelGGL((tsp::attn_merge_kernel<uint16_t, 128>), grid, dim3(256), 0, st, mp); break;
+      case 256: hipLaunchKernelGGL((tsp::attn_merge_kernel<uint16_t, 256>), grid, dim3(256), 0, st, mp); break;
+    }
+  } else {
+    switch (dh) {
+      case 64: hipLaunchKernelGGL((tsp::attn_merge_kernel<float, 64>), grid, dim3(256), 0, st, mp); break;
+      case 128: hipLaunchKernelGGL((tsp::attn_merge_kernel<float, 128>), grid, dim3(256), 0, st, mp); break;
+      case 256: hipLaunchKernelGGL((tsp::attn_merge_kernel<float, 256>), grid, dim3(256), 0, st, mp); break;
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TSP_ELAUNCH, "merge kernel launch failed: %s", hipGetErrorString(e));
   g_last_error[0] = '\0';
   return TSP_OK;
 }

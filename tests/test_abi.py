@@ -45,8 +45,13 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_library_links_no_torch():
-    out = subprocess.run(["ldd", tsp.LIB_PATH], capture_output=True, text=True)
-    assert "torch" not in out.stdout and "c10" not in out.stdout
+    # the DT_NEEDED names (ldd would also print resolved paths, which may sit under
+    # torch's own library folder when LD_LIBRARY_PATH points there)
+    out = subprocess.run(["readelf", "-d", tsp.LIB_PATH], capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
+    deps = [ln.split("[")[1].split("]")[0] for ln in out.stdout.splitlines() if "(NEEDED)" in ln]
+    assert "libamdhip64.so.7" in deps or any(d.startswith("libamdhip64") for d in deps), deps
+    assert not [d for d in deps if "torch" in d or "c10" in d], deps
 
 
 MAP_CASES = [(2, 1, 0), (8, 4, 3), (512, 4, 1), (1200, 3, 2), (32768, 8, 3), (262144, 8, 0), (262144, 8, 7),
@@ -118,6 +123,54 @@ def test_null_and_misaligned_pointers_rejected(lib):
         assert _call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
         ptrs[i] = _fake(0x100008)
         assert _call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
+
+
+@pytest.mark.parametrize("lo,hi", [(10, 9), (-1, 5), (0, 513), (600, 700), (-5, -1)])
+def test_range_outside_sequence_rejected(lib, lo, hi):
+    a = VALID
+    f = _fake()
+    st = lib.tsp_attn_fwd_range(f, f, f, f, f, a["B"], a["S_total"], a["D"], a["rank"], a["Hq"], a["Hkv"], a["dh"],
+                                lo, hi, a["dtype"], None)
+    assert st == tsp.TSP_EINVAL
+    assert "range" in lib.tsp_attn_last_error().decode()
+
+
+def test_range_shares_fwd_validation(lib):
+    f = _fake()
+    assert lib.tsp_attn_fwd_range(f, f, f, f, None, 1, 512, 4, 1, 4, 1, 64, 0, 512, tsp.TSP_F32, None) == tsp.TSP_EINVAL
+    assert lib.tsp_attn_fwd_range(f, f, f, f, f, 1, 512, 4, 1, 4, 1, 96, 0, 512, tsp.TSP_F32, None) == \
+        tsp.TSP_EUNSUPPORTED
+
+
+MERGE_VALID = dict(B=1, S_local=128, Hq=4, dh=128, dtype=tsp.TSP_BF16)
+
+
+def _merge_call(lib, ptrs=None, **kw):
+    a = dict(MERGE_VALID)
+    a.update(kw)
+    p = ptrs if ptrs is not None else [_fake()] * 6
+    return lib.tsp_attn_merge(*p, a["B"], a["S_local"], a["Hq"], a["dh"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), tsp.TSP_EINVAL),
+    (dict(S_local=0), tsp.TSP_EINVAL),
+    (dict(Hq=0), tsp.TSP_EINVAL),
+    (dict(dh=96), tsp.TSP_EUNSUPPORTED),
+    (dict(dtype=5), tsp.TSP_EUNSUPPORTED),
+])
+def test_merge_invalid_arguments_rejected(lib, kw, code):
+    assert _merge_call(lib, **kw) == code
+    assert lib.tsp_attn_last_error().decode() != ""
+
+
+def test_merge_null_and_misaligned_pointers_rejected(lib):
+    for i in range(6):
+        ptrs = [_fake()] * 6
+        ptrs[i] = None
+        assert _merge_call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
+        ptrs[i] = _fake(0x100004)
+        assert _merge_call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
 
 
 def test_map_helpers_reject_bad_sizes(lib):

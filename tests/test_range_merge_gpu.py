@@ -1,0 +1,249 @@
+"""Key-range attention and the log-sum-exp merge (tsp_attn_fwd_range, tsp_attn_merge) vs
+the fp64 oracle, through the C ABI, on an MI355X (gfx950).
+
+A rank that overlaps the K/V all-gather with compute attends to each gathered chunk as it
+arrives and merges the partials; the result must equal attention over the full K/V.
+Tolerances as in the full-path parity tests: max-abs 2e-2 (bf16) / 1e-4 (fp32) on out and
+lse, plus a relative Frobenius bound of 1e-2 for bf16. Rows with no visible key in the
+range must come back exactly as out = 0, lse = -inf.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sequence_causal_attention_amd as tsp
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+DEV = "cuda:0"
+
+
+def _note(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_partial(out, lse, ref_out, ref_lse, dtype):
+    """Exact empties, then the tolerance on every row with a visible key."""
+    tol = TOL[dtype]
+    empty = np.isneginf(ref_lse)  # [B, Hq, rows]
+    assert np.array_equal(np.isneginf(lse), empty), "empty rows differ"
+    e_rows = empty.transpose(0, 2, 1)  # [B, rows, Hq]
+    assert (out[e_rows] == 0).all(), "an empty row has a nonzero output"
+    assert np.isfinite(out).all()
+    if (~empty).any():
+        err_l = np.abs(lse[~empty] - ref_lse[~empty]).max()
+        assert err_l <= tol, f"max |lse - ref| = {err_l:.3g}"
+    err_o = np.abs(out - ref_out).max()
+    assert err_o <= tol, f"max |out - ref| = {err_o:.3g}"
+    if dtype == torch.bfloat16 and (~e_rows).any():
+        d = (out - ref_out)[~e_rows]
+        rel = np.linalg.norm(d) / max(np.linalg.norm(ref_out[~e_rows]), 1e-30)
+        assert rel <= 1e-2, f"relative error {rel:.3g}"
+
+
+RANGE_CASES = [  # (B, S_total, D, rank, Hq, Hkv, dh, dtype, kv_begin, kv_end)
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, 0, 2048),      # whole range
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, 384, 512),     # one aligned gathered chunk
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, 100, 1700),    # unaligned both ends
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, 1600, 1700),   # only the second chunk sees it
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, 1900, 2048),   # beyond every position: empty
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, 700, 700),     # empty range
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, 417, 418),     # a single key
+    (1, 2048, 8, 0, 4, 4, 128, torch.bfloat16, 33, 95),       # inside the first chunk's diagonal
+    (1, 4096, 4, 2, 12, 2, 256, torch.bfloat16, 1000, 2600),  # GQA, dh 256
+    (1, 1024, 2, 1, 8, 2, 64, torch.bfloat16, 250, 777),      # dh 64
+    (1, 1200, 3, 2, 6, 2, 128, torch.bfloat16, 399, 801),     # ragged chunks
+    (1, 4096, 1, 0, 4, 4, 128, torch.bfloat16, 1024, 3000),   # D = 1
+    (2, 1024, 4, 1, 4, 2, 128, torch.bfloat16, 128, 896),     # batch of 2
+    (1, 512, 4, 1, 4, 1, 64, torch.float32, 64, 448),         # fp32
+    (1, 600, 3, 1, 2, 1, 128, torch.float32, 37, 451),        # fp32 ragged, unaligned
+    (1, 288, 2, 1, 4, 2, 256, torch.float32, 100, 101),       # fp32 single key
+    (1, 512, 4, 1, 4, 1, 64, torch.float32, 300, 300),        # fp32 empty range
+    # a wave whose rows are partly empty (row 32 sees none of keys 33..94, row 33 does):
+    # the running-max update must leave the empty rows at zero
+    (1, 512, 4, 0, 4, 1, 64, torch.float32, 33, 95),
+    (1, 1024, 2, 0, 8, 2, 64, torch.bfloat16, 45, 46),
+]
+
+
+@pytest.mark.parametrize("case", RANGE_CASES,
+                         ids=lambda c: "B{}_S{}_D{}_r{}_H{}x{}_d{}_{}_{}-{}".format(*c[:7], str(c[7])[6:], *c[8:]))
+def test_range_vs_oracle(case):
+    B, S, D, r, Hq, Hkv, dh, dtype, lo, hi = case
+    _note(f"range {case}")
+    q, k, v = workloads.make_custom(B, S, D, Hq, Hkv, dh, dtype, seed=11)
+    out, lse = tsp.fwd(q.to(DEV), k.to(DEV), v.to(DEV), D=D, rank=r, kv_range=(lo, hi))
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.causal_attention_range(q, k, v, D, r, lo, hi)
+    check_partial(_np(out), _np(lse), ref_out, ref_lse, dtype)
+
+
+def test_full_range_is_bitwise_fwd():
+    _note("full range == fwd")
+    q, k, v = workloads.make_custom(1, 2048, 8, 4, 4, 128, torch.bfloat16, seed=5)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o1, l1 = tsp.fwd(qd, kd, vd, D=8, rank=3)
+    o2, l2 = tsp.fwd(qd, kd, vd, D=8, rank=3, kv_range=(0, 2048))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _chunk_pipeline(qd, kd, vd, D, r, bounds):
+    """Attend to each key chunk in turn and merge into a running (out, lse) in place."""
+    acc_o = acc_l = None
+    part_o, part_l = torch.empty_like(qd), None
+    for lo, hi in bounds:
+        if acc_o is None:
+            acc_o, acc_l = tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=(lo, hi))
+            part_l = torch.empty_like(acc_l)
+            continue
+        tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=(lo, hi), out=part_o, lse=part_l)
+        tsp.merge(acc_o, acc_l, part_o, part_l, out=acc_o, lse=acc_l)
+    torch.cuda.synchronize()
+    return acc_o, acc_l
+
+
+PIPE_CASES = [  # (B, S_total, D, rank, Hq, Hkv, dh, dtype, order)
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, "ring"),     # arrival order of a ring from rank r
+    (1, 2048, 8, 0, 4, 4, 128, torch.bfloat16, "natural"),
+    (1, 2048, 8, 7, 4, 4, 128, torch.bfloat16, "reverse"),
+    (1, 4096, 4, 2, 12, 2, 256, torch.bfloat16, "ring"),
+    (1, 1024, 2, 1, 8, 2, 64, torch.bfloat16, "ring"),
+    (1, 1200, 3, 2, 6, 2, 128, torch.bfloat16, "ring"),     # ragged: chunks of 200 keys
+    (1, 512, 4, 1, 4, 1, 64, torch.float32, "ring"),
+    (1, 600, 3, 1, 2, 1, 128, torch.float32, "reverse"),
+]
+
+
+def _bounds(S, D, r, order):
+    C = S // (2 * D)
+    chunks = list(range(2 * D))
+    if order == "ring":  # own chunks first, then the others as a ring all-gather delivers them
+        chunks = sorted(chunks, key=lambda c: ((c % D - r) % D, c))
+    elif order == "reverse":
+        chunks = chunks[::-1]
+    return [(c * C, (c + 1) * C) for c in chunks]
+
+
+@pytest.mark.parametrize("case", PIPE_CASES,
+                         ids=lambda c: "B{}_S{}_D{}_r{}_H{}x{}_d{}_{}_{}".format(*c[:7], str(c[7])[6:], c[8]))
+def test_chunk_pipeline_merge(case):
+    B, S, D, r, Hq, Hkv, dh, dtype, order = case
+    _note(f"pipeline {case}")
+    q, k, v = workloads.make_custom(B, S, D, Hq, Hkv, dh, dtype, seed=23)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    bounds = _bounds(S, D, r, order)
+    assert sorted(bounds) == [(c * (S // (2 * D)), (c + 1) * (S // (2 * D))) for c in range(2 * D)]
+    o, l = _chunk_pipeline(qd, kd, vd, D, r, bounds)
+    ref_out, ref_lse = oracle.causal_attention(q, k, v, D, r)
+    out, lse = _np(o), _np(l)
+    assert np.isfinite(lse).all()
+    check_partial(out, lse, ref_out, ref_lse, dtype)
+    # and against the single-launch kernel
+    of, lf = tsp.fwd(qd, kd, vd, D=D, rank=r)
+    torch.cuda.synchronize()
+    assert np.abs(out - _np(of)).max() <= TOL[dtype]
+    # bf16: each form sums weights rounded to bf16 (relative error <= 2^-9 per weight), so
+    # each lse is within 2^-9 of exact and the two within 2^-8 of each other
+    assert np.abs(lse - _np(lf)).max() <= (2.0 ** -8 if dtype == torch.bfloat16 else 1e-5)
+
+
+def test_chunk_pipeline_workload_sampled():
+    """The 7B shard at its full size, gathered in 16 chunks, on sampled rows."""
+    w = workloads.BY_NAME["tsp_7b_shard_s32k"]
+    r = w.ranks[0]
+    _note(f"pipeline workload {w.name} rank {r}")
+    q, k, v = workloads.make_inputs(w, r)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, l = _chunk_pipeline(qd, kd, vd, w.D, r, _bounds(w.S_total, w.D, r, "ring"))
+    C = w.S_total // (2 * w.D)
+    rows = np.concatenate([np.arange(0, 48), np.arange(C - 16, C + 32), np.arange(2 * C - 16, 2 * C)])
+    heads = [0, 17, 31]
+    ref_out, ref_lse = oracle.causal_attention(q, k, v, w.D, r, rows=rows, heads=heads)
+    idx = torch.as_tensor(rows, device=DEV)
+    hidx = torch.as_tensor(heads, device=DEV)
+    out = _np(o.index_select(1, idx).index_select(2, hidx))
+    lse = _np(l.index_select(1, hidx).index_select(2, idx))
+    check_partial(out, lse, ref_out, ref_lse, w.torch_dtype())
+
+
+MERGE_CASES = [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.bfloat16, 256), (torch.float32, 64),
+               (torch.float32, 128), (torch.float32, 256)]
+
+
+def _merge_inputs(dtype, dh, B=2, S_local=96, Hq=3, seed=7):
+    g = torch.Generator().manual_seed(seed)
+    oa = torch.randn(B, S_local, Hq, dh, generator=g).to(dtype)
+    ob = torch.randn(B, S_local, Hq, dh, generator=g).to(dtype)
+    la = torch.randn(B, Hq, S_local, generator=g) * 4
+    lb = torch.randn(B, Hq, S_local, generator=g) * 4
+    # empties: a alone, b alone, both; a huge lse gap
+    la[0, 0, :10] = -float("inf")
+    lb[0, 1, 5:15] = -float("inf")
+    la[1, 2, 20:30] = -float("inf")
+    lb[1, 2, 20:30] = -float("inf")
+    la[1, 0, 40:50] = 80.0
+    lb[1, 0, 40:50] = -80.0
+    # an empty partial comes back as out = 0
+    oa.permute(0, 2, 1, 3)[torch.isneginf(la)] = 0
+    ob.permute(0, 2, 1, 3)[torch.isneginf(lb)] = 0
+    return oa, la, ob, lb
+
+
+@pytest.mark.parametrize("dtype,dh", MERGE_CASES, ids=lambda x: str(x))
+@pytest.mark.parametrize("inplace", [False, True])
+def test_merge_vs_oracle(dtype, dh, inplace):
+    _note(f"merge {dtype} dh{dh} inplace={inplace}")
+    oa, la, ob, lb = _merge_inputs(dtype, dh)
+    ref_o, ref_l = oracle.merge_partials(oa, la, ob, lb)
+    a_o, a_l, b_o, b_l = (t.to(DEV) for t in (oa, la, ob, lb))
+    if inplace:
+        o, l = tsp.merge(a_o, a_l, b_o, b_l, out=a_o, lse=a_l)
+        assert o.data_ptr() == a_o.data_ptr()
+    else:
+        o, l = tsp.merge(a_o, a_l, b_o, b_l)
+    torch.cuda.synchronize()
+    out, lse = _np(o), _np(l)
+    both = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(lse), both)
+    assert (out[both.transpose(0, 2, 1)] == 0).all()
+    assert np.abs(lse[~both] - ref_l[~both]).max() <= 1e-5
+    # bf16: one rounding of a convex combination of bf16 values
+    tol = 1e-5 if dtype == torch.float32 else 2 ** -8 * np.abs(ref_o).max()
+    assert np.abs(out - ref_o).max() <= tol
+
+
+def test_merge_inputs_untouched_and_canaries():
+    _note("merge canaries")
+    oa, la, ob, lb = _merge_inputs(torch.bfloat16, 128)
+    a_o, a_l, b_o, b_l = (t.to(DEV) for t in (oa, la, ob, lb))
+    big = torch.full((a_o.numel() + 64,), 7.0, dtype=a_o.dtype, device=DEV)
+    out = big[:a_o.numel()].view_as(a_o)
+    bigl = torch.full((a_l.numel() + 64,), 7.0, device=DEV)
+    lse = bigl[:a_l.numel()].view_as(a_l)
+    tsp.merge(a_o, a_l, b_o, b_l, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert (big[a_o.numel():] == 7).all() and (bigl[a_l.numel():] == 7).all()
+    assert torch.equal(a_o.cpu(), oa) and torch.equal(b_l.cpu(), lb)
+
+
+def test_range_invalid_arguments_write_nothing():
+    _note("range invalid")
+    q, k, v = workloads.make_custom(1, 512, 4, 4, 1, 64, torch.bfloat16, seed=3)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.full_like(qd, 5.0)
+    lse = torch.full((1, 4, 128), 5.0, device=DEV)
+    for lo, hi in [(10, 9), (-1, 5), (0, 513), (600, 700)]:
+        with pytest.raises(tsp.TspAttnError) as ei:
+            tsp.fwd(qd, kd, vd, D=4, rank=1, kv_range=(lo, hi), out=out, lse=lse)
+        assert ei.value.status == tsp.TSP_EINVAL
+    torch.cuda.synchronize()
+    assert (out == 5).all() and (lse == 5).all()
