@@ -98,9 +98,10 @@ def main():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--chunk-pipeline", action="store_true",
+    ap.add_argument("--chunk-pipeline", nargs="?", const="fused", choices=["fused", "merge"], default=None,
                     help="time the chunk-pipelined form instead: one key-range launch per gathered "
-                         "chunk (2D of them, in ring arrival order) merged into the running result")
+                         "chunk (2D of them, in ring arrival order), folded into the running result "
+                         "in the kernel's epilogue (fused, the default) or by a separate merge launch")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run plain device copies of MIB MiB (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -149,8 +150,12 @@ def main():
             return
         tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream, kv_range=bounds[0])
         for rng in bounds[1:]:
-            tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=part_o, lse=part_l, stream=stream, kv_range=rng)
-            tsp.merge(out, lse, part_o, part_l, out=out, lse=lse, stream=stream)
+            if args.chunk_pipeline == "fused":
+                tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream, kv_range=rng,
+                        accumulate=True)
+            else:
+                tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=part_o, lse=part_l, stream=stream, kv_range=rng)
+                tsp.merge(out, lse, part_o, part_l, out=out, lse=lse, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -196,8 +201,10 @@ def main():
             "workload": w.name, "B": w.B, "S_total": w.S_total, "D": w.D, "rank": rank, "Hq": w.Hq,
             "Hkv": w.Hkv, "dh": w.dh, "local_queries": w.S_local, "flops_per_step": flops,
             "parallelism": "one sequence-parallel rank's shard on 1 GPU",
-            "form": (f"chunk pipeline: {len(bounds)} key-range launches + {len(bounds) - 1} merges"
-                     if args.chunk_pipeline else "single launch"),
+            "form": ("single launch" if not args.chunk_pipeline else
+                     f"chunk pipeline: {len(bounds)} key-range launches, merged in the epilogue"
+                     if args.chunk_pipeline == "fused" else
+                     f"chunk pipeline: {len(bounds)} key-range launches + {len(bounds) - 1} merge launches"),
         },
         "roofline": {
             "bound": "mfma",

@@ -81,19 +81,24 @@ int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, vo
 
 /*
  * tsp_attn_fwd_range -- tsp_attn_fwd restricted to the keys j in [kv_begin, kv_end)
- * (0 <= kv_begin <= kv_end <= S_total), still causal by global position. A local row
- * with no visible key in the range gets out = 0 and lse = -inf. Partials over disjoint
- * ranges combine exactly with tsp_attn_merge, so a rank can attend to each gathered
- * chunk of K/V as it arrives ("Folding Tensor and Sequence Parallelism ...", section 2,
- * attention layers: the all-gather along the sequence; section 3 item 3: communication
- * overlapped with compute). Only keys in [kv_begin rounded down to 64, kv_end) and below
- * the rank's last position are read. Same arguments, layouts, ownership and errors as
- * tsp_attn_fwd, plus TSP_EINVAL for a range outside [0, S_total].
+ * (0 <= kv_begin <= kv_end <= S_total), still causal by global position, so that a rank
+ * can attend to each gathered chunk of K/V as it arrives ("Folding Tensor and Sequence
+ * Parallelism ...", section 2, attention layers: the all-gather along the sequence;
+ * section 3 item 3: communication overlapped with compute).
+ *   accumulate = 0: out / lse receive the partial result over the range; a local row with
+ *                   no visible key in the range gets out = 0 and lse = -inf.
+ *   accumulate = 1: out / lse already hold a result over keys disjoint from the range
+ *                   (lse = -inf where that result has no key); the partial is merged into
+ *                   them with the tsp_attn_merge rule in the kernel's epilogue, and rows
+ *                   with no visible key in the range are left untouched.
+ * Only keys in [kv_begin rounded down to 64, kv_end) and below the rank's last position
+ * are read. Same arguments, layouts, ownership and errors as tsp_attn_fwd, plus
+ * TSP_EINVAL for a range outside [0, S_total] or accumulate not in {0, 1}.
  */
 int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_full, void* out,
                        float* lse, int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq,
-                       int64_t Hkv, int64_t dh, int64_t kv_begin, int64_t kv_end, int dtype,
-                       void* stream);
+                       int64_t Hkv, int64_t dh, int64_t kv_begin, int64_t kv_end, int accumulate,
+                       int dtype, void* stream);
 
 /*
  * tsp_attn_merge -- combine two partial results over disjoint key sets:

@@ -38,7 +38,7 @@ SIGNATURES = {
     "tsp_attn_fwd": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                     ctypes.c_int, _VP]),
     "tsp_attn_fwd_range": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
-                                          _I64, _I64, ctypes.c_int, _VP]),
+                                          _I64, _I64, ctypes.c_int, ctypes.c_int, _VP]),
     "tsp_attn_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "tsp_attn_zigzag_positions": (ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(_I64)]),
     "tsp_attn_zigzag_positions_device": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP]),
@@ -90,14 +90,17 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D: int, rank: int,
-        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None, kv_range=None):
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None, kv_range=None,
+        accumulate: bool = False):
     """Causal attention of this rank's zigzag queries against the full K/V.
 
     q_local [B, 2C, Hq, dh], k_full / v_full [B, S_total, Hkv, dh]: contiguous, same
     device and dtype (bf16 or fp32). Returns (out [B, 2C, Hq, dh] same dtype,
     lse [B, Hq, 2C] fp32). ``out`` / ``lse`` may be passed in preallocated.
     ``kv_range=(begin, end)`` restricts the keys (tsp_attn_fwd_range): rows without a
-    visible key in the range get out = 0, lse = -inf.
+    visible key in the range get out = 0, lse = -inf. With ``accumulate=True`` the
+    partial over the range is merged into the ``out`` / ``lse`` passed in (a result over
+    disjoint keys) instead of overwriting them.
     The call is asynchronous on ``stream`` (default: the current stream).
     """
     for name, t in (("q_local", q_local), ("k_full", k_full), ("v_full", v_full)):
@@ -118,6 +121,8 @@ def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D:
     if D < 1 or S_total % (2 * D) != 0 or S_local != S_total // D:
         raise TspAttnError(TSP_EINVAL, f"q_local must hold S_total / D = {S_total // max(D, 1)} rows")
     code = _dtype_code(q_local)
+    if accumulate and (out is None or lse is None):
+        raise TspAttnError(TSP_EINVAL, "accumulate needs the running out and lse")
     if out is None:
         out = torch.empty_like(q_local)
     if lse is None:
@@ -132,7 +137,8 @@ def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D:
     lo, hi = (0, S_total) if kv_range is None else (int(kv_range[0]), int(kv_range[1]))
     with torch.cuda.device(q_local.device):
         st = lib().tsp_attn_fwd_range(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
-                                      lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, lo, hi, code, handle)
+                                      lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, lo, hi, int(bool(accumulate)),
+                                      code, handle)
     _check(st)
     return out, lse
 

@@ -33,8 +33,10 @@ struct TspParams {
   int32_t n_hgroups;     // grp / GH
   int32_t n_units;       // B * Hkv * n_hgroups * n_pairs workgroups
   int32_t kv_lo, kv_hi;  // only keys in [kv_lo, kv_hi) take part (whole sequence: 0, S_total)
+  int32_t accumulate;    // 0: write (out, lse); 1: merge into the (out, lse) already there
   float scale_log2;      // log2(e) / sqrt(dh): scores go straight to the exp2 domain
 };
+
 
 // Workgroup -> work unit. Workgroups are dispatched round-robin over the 8 XCDs
 // (block id b lands on XCD b % 8); consecutive units share a KV head, so give each XCD a
@@ -72,6 +74,26 @@ __device__ __forceinline__ float tsp_sum_bf16_pair(uint32_t packed, float acc) {
 
 // Units of the lse store: natural log from the base-2 running max and sum.
 constexpr float TSP_LN2 = 0.693147180559945309f;
+
+constexpr float TSP_LOG2E = 1.44269504088896340736f;
+
+// Weights of the log-sum-exp merge of a running result (lse_old, natural log, -inf when
+// it has no key yet) with a new partial whose lse is m2 + log2(l) in base 2 (l > 0).
+// Returns the new natural-log lse; w_old scales the old output, w_new the new partial's
+// unnormalised accumulator (1/l folded in).
+__device__ __forceinline__ float tsp_merge_weights(float lse_old, float m2, float l, float& w_old,
+                                                   float& w_new) {
+  const float old2 = lse_old * TSP_LOG2E;  // -inf stays -inf
+  const float new2 = m2 + __builtin_amdgcn_logf(l);
+  const float m = fmaxf(old2, new2);
+  const float e_old = old2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(old2 - m);
+  const float e_new = __builtin_amdgcn_exp2f(new2 - m);
+  const float tot = e_old + e_new;
+  const float inv = 1.0f / tot;
+  w_old = e_old * inv;
+  w_new = e_new * inv / l;
+  return (m + __builtin_amdgcn_logf(tot)) * TSP_LN2;
+}
 
 // The running max is only raised when a tile's max exceeds it by more than this many
 // base-2 units, so most tiles skip rescaling the accumulators; the unnormalised weights

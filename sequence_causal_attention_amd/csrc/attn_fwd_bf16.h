@@ -246,6 +246,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     const int32_t u_left = (kv_lo_rel + BK - 1) / BK;
 
     if (kv_end <= kv_lo_rel) {  // no key of the range is visible to any row of the tile
+      if (p.accumulate) continue;  // an empty partial leaves the running result as it is
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (rvalid[rb]) {
@@ -537,6 +538,33 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     }
 
     // ---- epilogue: normalise, round to bf16, write O and lse -----------------------------
+    if (p.accumulate) {  // merge this partial into the running result (out, lse)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float l = tsp_sum_halves(l_run[rb]);
+        if (!rvalid[rb] || !(l > 0.f)) continue;  // no visible key: nothing to add
+        float* lp = p.lse + ((int64_t)b * p.Hq + head[rb]) * p.S_local + lrow[rb];
+        float w_old, w_new;
+        const float lse_new = tsp_merge_weights(*lp, m_run[rb], l, w_old, w_new);
+        uint16_t* op = og + (((int64_t)b * p.S_local + lrow[rb]) * p.Hq + head[rb]) * DH + 4 * half;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            tsp_u32x2* dst = reinterpret_cast<tsp_u32x2*>(op + db * 32 + 8 * a);
+            const tsp_u32x2 o = *dst;
+            tsp_u32x2 w;
+            w[0] = tsp_pack_bf16(fmaf(w_new, acc[rb][db][4 * a + 0], w_old * __uint_as_float(o[0] << 16)),
+                                 fmaf(w_new, acc[rb][db][4 * a + 1], w_old * __uint_as_float(o[0] & 0xffff0000u)));
+            w[1] = tsp_pack_bf16(fmaf(w_new, acc[rb][db][4 * a + 2], w_old * __uint_as_float(o[1] << 16)),
+                                 fmaf(w_new, acc[rb][db][4 * a + 3], w_old * __uint_as_float(o[1] & 0xffff0000u)));
+            *dst = w;
+          }
+        // both halves of the wave have read the old lse above (the weights depend on it)
+        if (half == 0) *lp = lse_new;
+      }
+      continue;
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float l = tsp_sum_halves(l_run[rb]);

@@ -155,7 +155,26 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(TspParams p) {
       }
     }
 
-    if (wave_active) {
+    if (wave_active && p.accumulate) {  // merge this partial into the running result
+      const float l = tsp_sum_halves(l_run);
+      if (rvalid && l > 0.f) {
+        float* lp = p.lse + ((int64_t)b * p.Hq + head) * p.S_local + lrow;
+        float w_old, w_new;
+        const float lse_new = tsp_merge_weights(*lp, m_run, l, w_old, w_new);
+        float* op = og + (((int64_t)b * p.S_local + lrow) * p.Hq + head) * DH + 4 * half;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            float4* dst = reinterpret_cast<float4*>(op + db * 32 + 8 * a);
+            const float4 o = *dst;
+            *dst = make_float4(fmaf(w_new, acc[db][4 * a], w_old * o.x), fmaf(w_new, acc[db][4 * a + 1], w_old * o.y),
+                               fmaf(w_new, acc[db][4 * a + 2], w_old * o.z),
+                               fmaf(w_new, acc[db][4 * a + 3], w_old * o.w));
+          }
+        if (half == 0) *lp = lse_new;  // both halves read the old lse above
+      }
+    } else if (wave_active) {
       const float l = tsp_sum_halves(l_run);
       const float inv = l > 0.f ? 1.0f / l : 0.f;  // l = 0: no visible key in the range
       if (rvalid) {

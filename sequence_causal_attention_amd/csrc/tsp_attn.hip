@@ -171,7 +171,7 @@ extern "C" {
 
 int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse,
                        int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh,
-                       int64_t kv_begin, int64_t kv_end, int dtype, void* stream) {
+                       int64_t kv_begin, int64_t kv_end, int accumulate, int dtype, void* stream) {
   if (!q_local || !k_full || !v_full || !out || !lse) return fail(TSP_EINVAL, "null pointer argument");
   if (!aligned16(q_local) || !aligned16(k_full) || !aligned16(v_full) || !aligned16(out) || !aligned16(lse))
     return fail(TSP_EINVAL, "pointers must be 16-byte aligned");
@@ -182,8 +182,10 @@ int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_fu
   if (kv_begin < 0 || kv_begin > kv_end || kv_end > S_total)
     return fail(TSP_EINVAL, "key range [%lld, %lld) not inside [0, %lld]", (long long)kv_begin,
                 (long long)kv_end, (long long)S_total);
+  if (accumulate != 0 && accumulate != 1) return fail(TSP_EINVAL, "accumulate must be 0 or 1");
   p.kv_lo = (int32_t)kv_begin;
   p.kv_hi = (int32_t)kv_end;
+  p.accumulate = accumulate;
   p.q = q_local;
   p.k = k_full;
   p.v = v_full;
@@ -213,8 +215,8 @@ int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_fu
 int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse, int64_t B,
                  int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
                  void* stream) {
-  return tsp_attn_fwd_range(q_local, k_full, v_full, out, lse, B, S_total, D, rank, Hq, Hkv, dh, 0, S_total, dtype,
-                            stream);
+  return tsp_attn_fwd_range(q_local, k_full, v_full, out, lse, B, S_total, D, rank, Hq, Hkv, dh, 0, S_total, 0,
+                            dtype, stream);
 }
 
 int tsp_attn_merge(const void* out_a, const float* lse_a, const void* out_b, const float* lse_b, void* out,

@@ -130,16 +130,19 @@ def test_range_outside_sequence_rejected(lib, lo, hi):
     a = VALID
     f = _fake()
     st = lib.tsp_attn_fwd_range(f, f, f, f, f, a["B"], a["S_total"], a["D"], a["rank"], a["Hq"], a["Hkv"], a["dh"],
-                                lo, hi, a["dtype"], None)
+                                lo, hi, 0, a["dtype"], None)
     assert st == tsp.TSP_EINVAL
     assert "range" in lib.tsp_attn_last_error().decode()
 
 
 def test_range_shares_fwd_validation(lib):
     f = _fake()
-    assert lib.tsp_attn_fwd_range(f, f, f, f, None, 1, 512, 4, 1, 4, 1, 64, 0, 512, tsp.TSP_F32, None) == tsp.TSP_EINVAL
-    assert lib.tsp_attn_fwd_range(f, f, f, f, f, 1, 512, 4, 1, 4, 1, 96, 0, 512, tsp.TSP_F32, None) == \
+    assert lib.tsp_attn_fwd_range(f, f, f, f, None, 1, 512, 4, 1, 4, 1, 64, 0, 512, 0, tsp.TSP_F32, None) == \
+        tsp.TSP_EINVAL
+    assert lib.tsp_attn_fwd_range(f, f, f, f, f, 1, 512, 4, 1, 4, 1, 96, 0, 512, 0, tsp.TSP_F32, None) == \
         tsp.TSP_EUNSUPPORTED
+    assert lib.tsp_attn_fwd_range(f, f, f, f, f, 1, 512, 4, 1, 4, 1, 64, 0, 512, 2, tsp.TSP_F32, None) == \
+        tsp.TSP_EINVAL
 
 
 MERGE_VALID = dict(B=1, S_local=128, Hq=4, dh=128, dtype=tsp.TSP_BF16)

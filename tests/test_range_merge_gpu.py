@@ -96,17 +96,20 @@ def test_full_range_is_bitwise_fwd():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def _chunk_pipeline(qd, kd, vd, D, r, bounds):
-    """Attend to each key chunk in turn and merge into a running (out, lse) in place."""
+def _chunk_pipeline(qd, kd, vd, D, r, bounds, fused):
+    """Attend to each key chunk in turn and fold it into a running (out, lse): in the
+    kernel's epilogue (fused) or with a separate merge launch."""
     acc_o = acc_l = None
     part_o, part_l = torch.empty_like(qd), None
     for lo, hi in bounds:
         if acc_o is None:
             acc_o, acc_l = tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=(lo, hi))
             part_l = torch.empty_like(acc_l)
-            continue
-        tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=(lo, hi), out=part_o, lse=part_l)
-        tsp.merge(acc_o, acc_l, part_o, part_l, out=acc_o, lse=acc_l)
+        elif fused:
+            tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=(lo, hi), out=acc_o, lse=acc_l, accumulate=True)
+        else:
+            tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=(lo, hi), out=part_o, lse=part_l)
+            tsp.merge(acc_o, acc_l, part_o, part_l, out=acc_o, lse=acc_l)
     torch.cuda.synchronize()
     return acc_o, acc_l
 
@@ -133,16 +136,17 @@ def _bounds(S, D, r, order):
     return [(c * C, (c + 1) * C) for c in chunks]
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "merge"])
 @pytest.mark.parametrize("case", PIPE_CASES,
                          ids=lambda c: "B{}_S{}_D{}_r{}_H{}x{}_d{}_{}_{}".format(*c[:7], str(c[7])[6:], c[8]))
-def test_chunk_pipeline_merge(case):
+def test_chunk_pipeline_merge(case, fused):
     B, S, D, r, Hq, Hkv, dh, dtype, order = case
-    _note(f"pipeline {case}")
+    _note(f"pipeline {case} fused={fused}")
     q, k, v = workloads.make_custom(B, S, D, Hq, Hkv, dh, dtype, seed=23)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     bounds = _bounds(S, D, r, order)
     assert sorted(bounds) == [(c * (S // (2 * D)), (c + 1) * (S // (2 * D))) for c in range(2 * D)]
-    o, l = _chunk_pipeline(qd, kd, vd, D, r, bounds)
+    o, l = _chunk_pipeline(qd, kd, vd, D, r, bounds, fused)
     ref_out, ref_lse = oracle.causal_attention(q, k, v, D, r)
     out, lse = _np(o), _np(l)
     assert np.isfinite(lse).all()
@@ -156,14 +160,15 @@ def test_chunk_pipeline_merge(case):
     assert np.abs(lse - _np(lf)).max() <= (2.0 ** -8 if dtype == torch.bfloat16 else 1e-5)
 
 
-def test_chunk_pipeline_workload_sampled():
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "merge"])
+def test_chunk_pipeline_workload_sampled(fused):
     """The 7B shard at its full size, gathered in 16 chunks, on sampled rows."""
     w = workloads.BY_NAME["tsp_7b_shard_s32k"]
     r = w.ranks[0]
-    _note(f"pipeline workload {w.name} rank {r}")
+    _note(f"pipeline workload {w.name} rank {r} fused={fused}")
     q, k, v = workloads.make_inputs(w, r)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    o, l = _chunk_pipeline(qd, kd, vd, w.D, r, _bounds(w.S_total, w.D, r, "ring"))
+    o, l = _chunk_pipeline(qd, kd, vd, w.D, r, _bounds(w.S_total, w.D, r, "ring"), fused)
     C = w.S_total // (2 * w.D)
     rows = np.concatenate([np.arange(0, 48), np.arange(C - 16, C + 32), np.arange(2 * C - 16, 2 * C)])
     heads = [0, 17, 31]
@@ -173,6 +178,41 @@ def test_chunk_pipeline_workload_sampled():
     out = _np(o.index_select(1, idx).index_select(2, hidx))
     lse = _np(l.index_select(1, hidx).index_select(2, idx))
     check_partial(out, lse, ref_out, ref_lse, w.torch_dtype())
+
+
+ACC_CASES = [  # (B, S_total, D, rank, Hq, Hkv, dh, dtype, first range, second range)
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, (0, 700), (700, 1800)),
+    (1, 2048, 8, 0, 4, 4, 128, torch.bfloat16, (60, 100), (0, 60)),       # first leaves rows empty
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, (1900, 2048), (100, 900)),  # first is empty for all
+    (1, 4096, 4, 2, 12, 2, 256, torch.bfloat16, (2000, 4096), (0, 2000)),
+    (1, 1024, 2, 1, 8, 2, 64, torch.bfloat16, (300, 301), (0, 300)),
+    (1, 600, 3, 1, 2, 1, 128, torch.float32, (37, 451), (451, 600)),
+    (1, 512, 4, 0, 4, 1, 64, torch.float32, (33, 95), (0, 33)),
+]
+
+
+@pytest.mark.parametrize("case", ACC_CASES, ids=lambda c: "S{}_D{}_r{}_d{}_{}_{}_{}".format(
+    c[1], c[2], c[3], c[6], str(c[7])[6:], *c[8:]))
+def test_accumulate_matches_oracle_merge(case):
+    """A range launch with accumulate=1 on top of another range's result equals the
+    oracle's merge of the two partials (empty rows: untouched / exact)."""
+    B, S, D, r, Hq, Hkv, dh, dtype, ra, rb = case
+    _note(f"accumulate {case}")
+    q, k, v = workloads.make_custom(B, S, D, Hq, Hkv, dh, dtype, seed=31)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, l = tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=ra)
+    tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=rb, out=o, lse=l, accumulate=True)
+    torch.cuda.synchronize()
+    oa, la = oracle.causal_attention_range(q, k, v, D, r, *ra)
+    ob, lb = oracle.causal_attention_range(q, k, v, D, r, *rb)
+    ref_o, ref_l = oracle.merge_partials(oa, la, ob, lb)
+    check_partial(_np(o), _np(l), ref_o, ref_l, dtype)
+
+
+def test_accumulate_needs_running_result():
+    q, k, v = workloads.make_custom(1, 512, 4, 4, 1, 64, torch.bfloat16, seed=3)
+    with pytest.raises(tsp.TspAttnError):
+        tsp.fwd(q.to(DEV), k.to(DEV), v.to(DEV), D=4, rank=1, kv_range=(0, 64), accumulate=True)
 
 
 MERGE_CASES = [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.bfloat16, 256), (torch.float32, 64),
