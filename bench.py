@@ -74,7 +74,7 @@ def cpu_baseline(w, rank, q, k, v, budget_s: float):
     while True:
         oracle.causal_attention(q, k, v, w.D, rank, rows=rows, heads=heads, block=128)
         done += 1
-        if time.perf_counter() - t0 >= budget_s or done >= 64:
+        if time.perf_counter() - t0 >= budget_s:
             break
     dt = (time.perf_counter() - t0) / done
     flops = 4.0 * w.B * len(heads) * w.dh * pairs

@@ -2,6 +2,7 @@
 
 from .attention import (  # noqa: F401
     causal_attention,
+    causal_attention_backward,
     causal_attention_bruteforce,
     causal_attention_range,
     causal_flops,

@@ -35,8 +35,10 @@ Inputs are upcast exactly to float64 (bf16 and fp32 values are exactly represent
 
 Parity is pinned by the ``-m "not gpu"`` tests in tests/test_oracle_pins.py (brute force,
 a library routine for the one-rank case, closed forms, the concatenation identity, the
-equal-pair-count identity and the lesson page's GQA head ownership); none of the
-functions below is "parity unpinned".
+equal-pair-count identity and the lesson page's GQA head ownership; for the backward,
+central finite differences of the forward, PyTorch autograd through its causal SDPA,
+the rank-partition identity and closed-form sums); none of the functions below is
+"parity unpinned".
 """
 
 from __future__ import annotations
@@ -269,3 +271,67 @@ def merge_partials(out_a, lse_a, out_b, lse_b):
     # weights are [B, Hq, rows]; outputs are [B, rows, Hq, dh]
     out = out_a * ta.transpose(0, 2, 1)[..., None] + out_b * tb.transpose(0, 2, 1)[..., None]
     return out, lse
+
+
+# --------------------------------------------------------------------------------------
+# The backward pass of the per-rank attention.
+# Both systems the pages describe train models ("Folding Tensor and Sequence Parallelism
+# for Memory-Efficient Transformer Training & Inference"; "AutoSP: Unlocking
+# Long-Context LLM Training ...", section 2.B: attention activations are recomputed in
+# the backward pass rather than kept). The backward of the forward above is its
+# gradient, by the chain rule through the softmax. With s_ij = scale * q_i . k_j on
+# visible pairs and P_ij = softmax_j(s_ij) (0 on masked pairs), for an upstream
+# gradient dO of out:
+#   dV_j  = sum_i P_ij dO_i
+#   dP_ij = dO_i . v_j
+#   dS_ij = P_ij (dP_ij - sum_l P_il dP_il)
+#   dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
+# dK and dV are this rank's partial gradients of the gathered full K/V: the all-gather's
+# adjoint is a reduce-scatter that adds up the partials of all ranks ("Tensor, pipeline
+# e sequence parallelism", section 01: row-parallel pieces sum partial results). The
+# query heads that share a KV head add their contributions to it.
+# --------------------------------------------------------------------------------------
+def causal_attention_backward(q, k, v, dout, D: int, rank: int, kv_heads=None, block: int = 256):
+    """Oracle backward for one rank.
+
+    q, dout: [B, S_local, Hq, dh]; k, v: [B, S_total, Hkv, dh].
+    kv_heads: optional subset of KV heads; the query heads of their groups are included.
+    Returns (dq [B, S_local, n_q, dh], dk [B, S_total, n_kv, dh], dv [B, S_total, n_kv, dh])
+    in float64, n_kv = len(kv_heads), n_q = n_kv * Hq / Hkv (query heads in group order).
+    Keys that no local row sees get dk = dv = 0.
+    """
+    q, dout = _as_f64(q), _as_f64(dout)
+    B, S_local, Hq, dh = q.shape
+    S_total, Hkv = k.shape[1], k.shape[2]
+    pos_all = zigzag_positions(S_total, D, rank)
+    if S_local != pos_all.shape[0] or dout.shape != q.shape:
+        raise ValueError("q_local and dout must hold 2 * S_total / (2D) rows")
+    kv_heads = list(range(Hkv)) if kv_heads is None else list(kv_heads)
+    grp = Hq // Hkv
+    scale = softmax_scale(dh)
+    dq = np.zeros((B, S_local, len(kv_heads) * grp, dh))
+    dk = np.zeros((B, S_total, len(kv_heads), dh))
+    dv = np.zeros((B, S_total, len(kv_heads), dh))
+    for b in range(B):
+        for ki, hk in enumerate(kv_heads):
+            kb, vb = _as_f64(k[b, :, hk, :]), _as_f64(v[b, :, hk, :])
+            for g in range(grp):
+                h = hk * grp + g
+                if kv_head_of(h, Hq, Hkv) != hk:
+                    raise ValueError("query head outside the KV head's group")
+                for start in range(0, S_local, block):
+                    r = np.arange(start, min(start + block, S_local))
+                    p = pos_all[r]
+                    nkeys = int(p.max()) + 1
+                    keys = np.arange(nkeys, dtype=np.int64)
+                    vis = visible(keys, p)
+                    s = np.where(vis, scale * (q[b, r, h, :] @ kb[:nkeys].T), -np.inf)
+                    e = np.exp(s - s.max(axis=1, keepdims=True))
+                    P = e / e.sum(axis=1, keepdims=True)  # softmax over the visible keys
+                    dO = dout[b, r, h, :]
+                    dP = dO @ vb[:nkeys].T
+                    dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                    dq[b, r, ki * grp + g, :] = scale * (dS @ kb[:nkeys])
+                    dk[b, :nkeys, ki, :] += scale * (dS.T @ q[b, r, h, :])
+                    dv[b, :nkeys, ki, :] += P.T @ dO
+    return dq, dk, dv

@@ -2,7 +2,9 @@
 
 Each ``pin_*`` takes an oracle namespace ``o`` (attributes ``causal_attention``,
 ``causal_attention_bruteforce``, ``zigzag_positions``, ``unmasked_pairs``,
-``kv_head_of``, ``causal_attention_range``, ``merge_partials``) and raises AssertionError when the implementation breaks the pin. The
+``kv_head_of``, ``causal_attention_range``, ``merge_partials``,
+``causal_attention_backward``) and raises AssertionError when the implementation breaks
+the pin. The
 same pins run against deliberately broken copies in test_oracle_mutants.py, which
 shows that a plausible mistake anywhere in the oracle trips at least one of them.
 """
@@ -281,6 +283,127 @@ def pin_merge_identity(o):
     assert np.allclose(m1[0], m2[0], rtol=0, atol=1e-15) and np.allclose(m1[1], m2[1], rtol=0, atol=1e-15)
 
 
+# -- the backward pass -------------------------------------------------------------------
+
+BWD_TINY = [  # (B, S_total, D, rank, Hq, Hkv, dh)
+    (1, 8, 2, 1, 2, 1, 4),    # zigzag, GQA 2:1
+    (1, 12, 3, 0, 1, 1, 3),   # rank 0 of 3 (holds the first and the last chunk)
+    (2, 8, 1, 0, 2, 2, 2),    # D = 1, batch of 2
+]
+
+
+def _bwd_inputs(case, seed):
+    B, S, D, r, Hq, Hkv, dh = case
+    q, k, v = _tiny_inputs(case, seed)
+    dout = _rand((B, S // D, Hq, dh), seed + 3)
+    return q, k, v, dout
+
+
+def pin_bwd_finite_differences(o):
+    """The backward is the derivative of the forward: central differences of
+    L = sum(out * dout) in every input element match dq, dk, dv."""
+    eps = 1e-6
+    for n, case in enumerate(BWD_TINY):
+        B, S, D, r, Hq, Hkv, dh = case
+        q, k, v, dout = _bwd_inputs(case, 40 + n)
+        dq, dk, dv = o.causal_attention_backward(q, k, v, dout, D, r, block=3)
+
+        def loss(qq, kk, vv):
+            return float(np.sum(o.causal_attention(qq, kk, vv, D, r)[0] * dout))
+
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert np.allclose(g, num, rtol=0, atol=1e-7), (case, name, np.abs(g - num).max())
+
+
+def pin_bwd_autograd_sdpa(o):
+    """D = 1: equals PyTorch autograd through its causal SDPA in fp64 (GQA by
+    repeat_interleave, whose adjoint sums the group's KV gradients)."""
+    for B, S, Hq, Hkv, dh, seed in [(1, 24, 2, 2, 8, 50), (2, 40, 6, 2, 16, 51), (1, 64, 4, 1, 32, 52)]:
+        q = _rand((B, S, Hq, dh), seed)
+        k = _rand((B, S, Hkv, dh), seed + 1)
+        v = _rand((B, S, Hkv, dh), seed + 2)
+        dout = _rand((B, S, Hq, dh), seed + 3)
+        dq, dk, dv = o.causal_attention_backward(q, k, v, dout, 1, 0, block=16)
+        grp = Hq // Hkv
+        tq = torch.from_numpy(q).requires_grad_()
+        tk = torch.from_numpy(k).requires_grad_()
+        tv = torch.from_numpy(v).requires_grad_()
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            tq.permute(0, 2, 1, 3), tk.permute(0, 2, 1, 3).repeat_interleave(grp, dim=1),
+            tv.permute(0, 2, 1, 3).repeat_interleave(grp, dim=1), is_causal=True)
+        ref.permute(0, 2, 1, 3).backward(torch.from_numpy(dout))
+        for got, t in ((dq, tq), (dk, tk), (dv, tv)):
+            assert np.allclose(got, t.grad.numpy(), rtol=0, atol=1e-10), (B, S, Hq, Hkv, dh)
+
+
+def pin_bwd_rank_partition(o):
+    """The ranks' partial dK/dV add up to the unsharded gradient, and their dQ rows,
+    scattered by global position, rebuild the unsharded dQ."""
+    for B, S, D, Hq, Hkv, dh, seed in [(1, 48, 3, 2, 1, 4, 60), (1, 64, 4, 4, 2, 8, 61), (2, 32, 2, 1, 1, 4, 62)]:
+        qf = _rand((B, S, Hq, dh), seed)
+        k = _rand((B, S, Hkv, dh), seed + 1)
+        v = _rand((B, S, Hkv, dh), seed + 2)
+        dof = _rand((B, S, Hq, dh), seed + 3)
+        fq, fk, fv = o.causal_attention_backward(qf, k, v, dof, 1, 0)
+        gq = np.full_like(fq, np.nan)
+        gk, gv = np.zeros_like(fk), np.zeros_like(fv)
+        for r in range(D):
+            pos = np.asarray(o.zigzag_positions(S, D, r))
+            dq, dk, dv = o.causal_attention_backward(qf[:, pos], k, v, dof[:, pos], D, r)
+            gq[:, pos] = dq
+            gk += dk
+            gv += dv
+        assert np.allclose(gq, fq, rtol=0, atol=1e-12), (S, D)
+        assert np.allclose(gk, fk, rtol=0, atol=1e-12), (S, D)
+        assert np.allclose(gv, fv, rtol=0, atol=1e-12), (S, D)
+
+
+def pin_bwd_closed_forms(o):
+    """Softmax rows sum to 1, so the dK of every KV head sums to 0 over the keys and its
+    dV sums to the group's total upstream gradient; dout = 0 gives zero gradients; equal
+    value rows give dq = dk = 0 (out no longer depends on the scores)."""
+    B, S, D, r, Hq, Hkv, dh = 1, 64, 4, 2, 6, 2, 8
+    q, k, v, dout = _bwd_inputs((B, S, D, r, Hq, Hkv, dh), 70)
+    dq, dk, dv = o.causal_attention_backward(q, k, v, dout, D, r, block=7)
+    assert np.allclose(dk.sum(axis=1), 0.0, rtol=0, atol=1e-12)
+    grp = Hq // Hkv
+    for hk in range(Hkv):
+        tot = dout[:, :, hk * grp:(hk + 1) * grp, :].sum(axis=(1, 2))
+        assert np.allclose(dv[:, :, hk, :].sum(axis=1), tot, rtol=0, atol=1e-12)
+    # keys past the rank's last position get nothing
+    last = int(np.asarray(o.zigzag_positions(S, D, r)).max())
+    assert np.all(dk[:, last + 1:] == 0) and np.all(dv[:, last + 1:] == 0)
+    z = o.causal_attention_backward(q, k, v, np.zeros_like(dout), D, r)
+    assert all(np.all(t == 0) for t in z)
+    vc = np.broadcast_to(_rand((B, 1, Hkv, dh), 71), v.shape).copy()
+    dq2, dk2, _ = o.causal_attention_backward(q, k, vc, dout, D, r)
+    assert np.allclose(dq2, 0.0, rtol=0, atol=1e-12) and np.allclose(dk2, 0.0, rtol=0, atol=1e-12)
+
+
+def pin_bwd_gqa_and_subset(o):
+    """GQA gradients equal the MHA gradients on repeated K/V with each group's dK/dV
+    summed; a subset of KV heads returns exactly those heads' slices."""
+    B, S, D, r, Hq, Hkv, dh = 1, 48, 3, 1, 6, 2, 4
+    q, k, v, dout = _bwd_inputs((B, S, D, r, Hq, Hkv, dh), 80)
+    grp = Hq // Hkv
+    dq, dk, dv = o.causal_attention_backward(q, k, v, dout, D, r)
+    mq, mk, mv = o.causal_attention_backward(q, np.repeat(k, grp, axis=2), np.repeat(v, grp, axis=2), dout, D, r)
+    assert np.allclose(dq, mq, rtol=0, atol=1e-12)
+    assert np.allclose(dk, mk.reshape(B, S, Hkv, grp, dh).sum(axis=3), rtol=0, atol=1e-12)
+    assert np.allclose(dv, mv.reshape(B, S, Hkv, grp, dh).sum(axis=3), rtol=0, atol=1e-12)
+    sq, sk, sv = o.causal_attention_backward(q, k, v, dout, D, r, kv_heads=[1])
+    assert np.array_equal(sq, dq[:, :, grp:2 * grp]) and np.array_equal(sk, dk[:, :, 1:2])
+    assert np.array_equal(sv, dv[:, :, 1:2])
+
+
 ALL_PINS = [
     pin_zigzag_golden,
     pin_zigzag_permutation,
@@ -298,4 +421,9 @@ ALL_PINS = [
     pin_range_bruteforce,
     pin_range_partition,
     pin_merge_identity,
+    pin_bwd_finite_differences,
+    pin_bwd_autograd_sdpa,
+    pin_bwd_rank_partition,
+    pin_bwd_closed_forms,
+    pin_bwd_gqa_and_subset,
 ]

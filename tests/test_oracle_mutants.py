@@ -3,7 +3,9 @@
 Every mutant is a copy of the oracle with one plausible error: a swapped or mirrored
 chunk, a strict causal diagonal, interleaved GQA grouping, a wrong softmax scale, a
 base-2 lse, a dropped normalisation, swapped K/V operands, local instead of global
-positions, or a block-boundary error in the blocked form.
+positions, or a block-boundary error in the blocked form; and, for the backward, a dropped
+softmax-Jacobian term, an unscaled dQ, a wrong operand or an overwritten GQA sum in dK,
+unnormalised weights in dV, or a strict diagonal.
 """
 
 import types
@@ -84,7 +86,8 @@ WRAPS = {
 def _namespace():
     ns = types.SimpleNamespace()
     for n in ("causal_attention", "causal_attention_bruteforce", "zigzag_positions",
-              "unmasked_pairs", "kv_head_of", "causal_attention_range", "merge_partials"):
+              "unmasked_pairs", "kv_head_of", "causal_attention_range", "merge_partials",
+              "causal_attention_backward"):
         setattr(ns, n, getattr(A, n))
     return ns
 
@@ -151,3 +154,69 @@ def test_blocked_form_error_is_caught():
     ns.causal_attention = _block_drops_last_row(A.causal_attention)
     failed = _failures(ns)
     assert "pin_bruteforce" in failed
+
+
+def _bwd_mutant(kind):
+    """A copy of the oracle's backward with one plausible mistake."""
+
+    def bwd(q, k, v, dout, D, rank, kv_heads=None, block=256):
+        q, dout, k, v = (np.asarray(x, dtype=np.float64) for x in (q, dout, k, v))
+        B, S_local, Hq, dh = q.shape
+        S_total, Hkv = k.shape[1], k.shape[2]
+        pos_all = A.zigzag_positions(S_total, D, rank)
+        kv_heads = list(range(Hkv)) if kv_heads is None else list(kv_heads)
+        grp = Hq // Hkv
+        scale = 1.0 / np.sqrt(dh)
+        dq = np.zeros((B, S_local, len(kv_heads) * grp, dh))
+        dk = np.zeros((B, S_total, len(kv_heads), dh))
+        dv = np.zeros((B, S_total, len(kv_heads), dh))
+        for b in range(B):
+            for ki, hk in enumerate(kv_heads):
+                kb, vb = k[b, :, hk, :], v[b, :, hk, :]
+                for g in range(grp):
+                    h = hk * grp + g
+                    for start in range(0, S_local, block):
+                        r = np.arange(start, min(start + block, S_local))
+                        p = pos_all[r]
+                        nkeys = int(p.max()) + 1
+                        keys = np.arange(nkeys)
+                        vis = keys[None, :] < p[:, None] if kind == "strict_diagonal" else keys[None, :] <= p[:, None]
+                        s = np.where(vis, scale * (q[b, r, h, :] @ kb[:nkeys].T), -np.inf)
+                        e = np.exp(s - s.max(axis=1, keepdims=True))
+                        P = e / e.sum(axis=1, keepdims=True)
+                        dO = dout[b, r, h, :]
+                        dP = dO @ vb[:nkeys].T
+                        if kind == "no_delta":
+                            dS = P * dP
+                        else:
+                            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                        dq[b, r, ki * grp + g, :] = (1.0 if kind == "dq_unscaled" else scale) * (dS @ kb[:nkeys])
+                        src = dO if kind == "dk_uses_dout" else q[b, r, h, :]
+                        if kind == "gqa_overwrite":
+                            dk[b, :nkeys, ki, :] = scale * (dS.T @ src)
+                        else:
+                            dk[b, :nkeys, ki, :] += scale * (dS.T @ src)
+                        dv[b, :nkeys, ki, :] += (e if kind == "dv_unnormalised" else P).T @ dO
+        return dq, dk, dv
+
+    return bwd
+
+
+BWD_MUTANTS = ["no_delta", "dq_unscaled", "dk_uses_dout", "gqa_overwrite", "dv_unnormalised", "strict_diagonal"]
+
+
+@pytest.mark.parametrize("kind", BWD_MUTANTS)
+def test_backward_mutant_is_caught(kind):
+    ns = _namespace()
+    ns.causal_attention_backward = _bwd_mutant(kind)
+    with np.errstate(all="ignore"):
+        failed = [f for f in _failures(ns) if f.startswith("pin_bwd")]
+    assert failed, f"backward mutant {kind} passed every backward pin"
+
+
+def test_backward_mutant_copy_is_faithful():
+    """Without a mistake the mutant copy passes the backward pins (so each failure above
+    comes from its one change)."""
+    ns = _namespace()
+    ns.causal_attention_backward = _bwd_mutant("none")
+    assert not [f for f in _failures(ns) if f.startswith("pin_bwd")]
