@@ -116,6 +116,35 @@ int tsp_attn_merge(const void* out_a, const float* lse_a, const void* out_b, con
                    int dtype, void* stream);
 
 /*
+ * tsp_attn_bwd -- backward of tsp_attn_fwd: the gradients of the rank's attention for an
+ * upstream gradient dout of out. The systems on the pages train models ("Folding Tensor
+ * and Sequence Parallelism for Memory-Efficient Transformer Training & Inference";
+ * "AutoSP ...", section 2.B: attention recomputed in the backward pass); with
+ * P_ij = exp(s_ij - lse_i) on visible pairs and delta_i = dout_i . out_i:
+ *   dv_j = sum_i P_ij dout_i,  dS_ij = P_ij (dout_i . v_j - delta_i),
+ *   dq_i = sum_j dS_ij k_j / sqrt(dh),  dk_j = sum_i dS_ij q_i / sqrt(dh).
+ *   q_local, k_full, v_full   the forward's inputs (layouts as in tsp_attn_fwd)
+ *   out, lse                  the forward's outputs for them
+ *   dout      device, [B, 2C, Hq, dh] contiguous, element type `dtype`
+ *   dq_local  device, [B, 2C, Hq, dh] (written)
+ *   dk_full   device, [B, S_total, Hkv, dh] (written), likewise dv_full: this rank's
+ *             partial gradients of the gathered K/V, summed over the query heads of each
+ *             KV head; the gradient of the full K/V is the sum of all ranks' partials (the
+ *             adjoint of the all-gather, a reduce-scatter). Keys that no local row sees
+ *             get 0.
+ *   delta     device, [B, Hq, 2C] float32 (written): dout_i . out_i per row and head
+ * dtype TSP_BF16 (TSP_F32 returns TSP_EUNSUPPORTED); outputs are the fp32 results
+ * rounded to nearest even. Same size rules as tsp_attn_fwd plus Hq * dh <= 2^22; all
+ * pointers non-NULL and 16-byte aligned, outputs not overlapping the inputs or each
+ * other. Enqueued on `stream`; returns TSP_OK, TSP_EINVAL, TSP_EUNSUPPORTED or
+ * TSP_ELAUNCH.
+ */
+int tsp_attn_bwd(const void* q_local, const void* k_full, const void* v_full, const void* out,
+                 const float* lse, const void* dout, void* dq_local, void* dk_full, void* dv_full,
+                 float* delta, int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq,
+                 int64_t Hkv, int64_t dh, int dtype, void* stream);
+
+/*
  * tsp_attn_zigzag_positions -- the zigzag map on the host: writes g(i) for the 2C local
  * rows of `rank` into out_host (caller-owned host memory of 2C int64).
  * ("Folding Tensor and Sequence Parallelism ...", section 2, zigzag partitioning.)

@@ -40,6 +40,7 @@ SIGNATURES = {
     "tsp_attn_fwd_range": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                           _I64, _I64, ctypes.c_int, ctypes.c_int, _VP]),
     "tsp_attn_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
+    "tsp_attn_bwd": (ctypes.c_int, [_VP] * 10 + [_I64] * 7 + [ctypes.c_int, _VP]),
     "tsp_attn_zigzag_positions": (ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(_I64)]),
     "tsp_attn_zigzag_positions_device": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP]),
     "tsp_attn_unmasked_pairs": (_I64, [_I64, _I64, _I64]),
@@ -168,6 +169,44 @@ def merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor, lse_b: 
                                   out.data_ptr(), lse.data_ptr(), B, S_local, Hq, dh, code, handle)
     _check(st)
     return out, lse
+
+
+def bwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, *, D: int, rank: int, dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Backward of ``fwd`` (tsp_attn_bwd): returns (dq [B, 2C, Hq, dh], dk, dv
+    [B, S_total, Hkv, dh] -- this rank's partial K/V gradients -- and delta [B, Hq, 2C]).
+    Outputs may be passed in preallocated. bf16 only."""
+    ins = (("q_local", q_local), ("k_full", k_full), ("v_full", v_full), ("out", out), ("dout", dout))
+    for name, t in ins + (("lse", lse),):
+        if not t.is_cuda or not t.is_contiguous():
+            raise TspAttnError(TSP_EINVAL, f"{name} must be a contiguous GPU tensor")
+    if not (q_local.dtype == k_full.dtype == v_full.dtype == out.dtype == dout.dtype):
+        raise TspAttnError(TSP_EINVAL, "q_local, k_full, v_full, out and dout must share one dtype")
+    if q_local.dim() != 4 or k_full.dim() != 4:
+        raise TspAttnError(TSP_EINVAL, "tensors must be 4-D [B, S, H, dh]")
+    B, S_local, Hq, dh = q_local.shape
+    _, S_total, Hkv, _ = k_full.shape
+    if v_full.shape != k_full.shape or out.shape != q_local.shape or dout.shape != q_local.shape:
+        raise TspAttnError(TSP_EINVAL, "shape mismatch between the forward's tensors")
+    if tuple(lse.shape) != (B, Hq, S_local) or lse.dtype != torch.float32:
+        raise TspAttnError(TSP_EINVAL, "lse must be float32 [B, Hq, S_local]")
+    code = _dtype_code(q_local)
+    dq = torch.empty_like(q_local) if dq is None else dq
+    dk = torch.empty_like(k_full) if dk is None else dk
+    dv = torch.empty_like(v_full) if dv is None else dv
+    delta = torch.empty_like(lse) if delta is None else delta
+    for name, t, ref in (("dq", dq, q_local), ("dk", dk, k_full), ("dv", dv, v_full), ("delta", delta, lse)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise TspAttnError(TSP_EINVAL, f"{name} must match {tuple(ref.shape)} {ref.dtype}")
+    if stream is None:
+        stream = torch.cuda.current_stream(q_local.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q_local.device):
+        st = lib().tsp_attn_bwd(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                delta.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, code, handle)
+    _check(st)
+    return dq, dk, dv, delta
 
 
 def fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, S_total, D, rank, Hq, Hkv, dh, dtype, stream) -> int:

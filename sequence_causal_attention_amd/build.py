@@ -1,7 +1,8 @@
 """Build the HIP library in-tree: ``python -m sequence_causal_attention_amd.build``.
 
-Compiles csrc/tsp_attn.hip for gfx950 into ``libtsp_attn.so`` next to this file.
-Packed fp32 VALU instructions are disabled for all device code.
+Compiles the translation units under csrc/ for gfx950 and links them into
+``libtsp_attn.so`` next to this file. Packed fp32 VALU instructions are disabled for all
+device code.
 """
 
 from __future__ import annotations
@@ -10,14 +11,29 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtsp_attn.so")
-SOURCES = [os.path.join(CSRC, "tsp_attn.hip")]
+# (source, flags of that translation unit only)
+UNITS = [
+    # forward kernels: MFMA results in arch VGPRs, the score tiles feed the VALU softmax
+    (os.path.join(CSRC, "tsp_attn.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
+    # backward kernels: the dK/dV accumulators live in the accumulation registers
+    (os.path.join(CSRC, "tsp_attn_bwd.hip"), []),
+]
+SOURCES = [u[0] for u in UNITS]
 HEADERS = [os.path.join(ROOT, "include", "tsp_attn.h")] + [
     os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".h")
+]
+COMMON = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++20",
+    "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
 
@@ -28,28 +44,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def command(out: str = LIB, extra=()) -> list:
-    return [
-        hipcc(),
-        "--offload-arch=gfx950",
-        "-O3",
-        "-std=c++20",
-        "-fPIC",
-        "-shared",
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA results in arch VGPRs: the score tiles feed VALU softmax directly
-        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-        "-I", os.path.join(ROOT, "include"),
-        "-I", CSRC,
-        *extra,
-        "-o", out,
-        *SOURCES,
-    ]
+def commands(out: str, objdir: str, extra=()) -> list:
+    """The compile command of every unit, then the link command."""
+    cmds, objs = [], []
+    for src, flags in UNITS:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmds.append([hipcc(), *COMMON, *flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra,
+                     "-c", "-o", obj, src])
+    cmds.append([hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", "-o", out, *objs])
+    return cmds
 
 
-def build(verbose: bool = True, extra=()) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp, extra)
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,6 +65,13 @@ def build(verbose: bool = True, extra=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
+
+
+def build(verbose: bool = True, extra=()) -> str:
+    tmp = LIB + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="tsp_attn_build_") as objdir:
+        for cmd in commands(tmp, objdir, extra):
+            _run(cmd, verbose)
     os.replace(tmp, LIB)
     return LIB
 

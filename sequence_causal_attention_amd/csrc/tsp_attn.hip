@@ -3,31 +3,25 @@
 // the error strings. The operation and every argument are documented in tsp_attn.h.
 #include <hip/hip_runtime.h>
 
-#include <cmath>
-#include <cstdarg>
-#include <cstdio>
-#include <cstdlib>
+#include <algorithm>
 
 #include "tsp_attn.h"
 #include "attn_common.h"
 #include "attn_fwd_bf16.h"
 #include "attn_fwd_f32.h"
 #include "attn_merge.h"
+#include "host_common.h"
+
+namespace tsp_host {
+thread_local char g_last_error[512] = "";
+}
 
 namespace {
 
-thread_local char g_last_error[512] = "";
-
-int fail(int status, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
-  va_end(ap);
-  if (std::getenv("TSP_ATTN_DEBUG")) std::fprintf(stderr, "tsp_attn: %s\n", g_last_error);
-  return status;
-}
-
-bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+using tsp_host::aligned16;
+using tsp_host::check_sizes;
+using tsp_host::fail;
+using tsp_host::KernelShape;
 
 // Tile configuration of the bf16 kernels per head dim: waves per workgroup, 32-row query
 // blocks per wave, depth of the LDS stage ring, target waves per SIMD.
@@ -62,13 +56,6 @@ struct Bf16Cfg<256> {
   static constexpr int NW = 4, RB = 1, NBUF = 4, SPS = 1, OCC = 1;
 };
 
-// Tile configuration of one (dtype, dh) kernel.
-struct KernelShape {
-  int kv_tile;     // keys per K/V tile
-  int waves;       // waves per workgroup
-  int row_blocks;  // 32-row query blocks per wave
-};
-
 template <int DH>
 KernelShape bf16_shape() {
   using C = Bf16Cfg<DH>;
@@ -91,60 +78,14 @@ bool kernel_shape(int dtype, int64_t dh, KernelShape* ks) {
   return false;
 }
 
-int check_sizes(int64_t S_total, int64_t D, int64_t rank) {
-  if (D < 1) return fail(TSP_EINVAL, "D must be >= 1 (got %lld)", (long long)D);
-  if (rank < 0 || rank >= D) return fail(TSP_EINVAL, "rank %lld outside [0, %lld)", (long long)rank, (long long)D);
-  if (S_total <= 0) return fail(TSP_EINVAL, "S_total must be > 0 (got %lld)", (long long)S_total);
-  if (S_total % (2 * D) != 0)
-    return fail(TSP_EINVAL, "S_total %lld not divisible by 2*D = %lld", (long long)S_total, (long long)(2 * D));
-  if (S_total > (int64_t(1) << 30)) return fail(TSP_EINVAL, "S_total %lld above 2^30", (long long)S_total);
-  return TSP_OK;
-}
-
 // Validates everything but pointers and builds the launch parameters.
 int plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
          TspParams* p, KernelShape* ks) {
   int st = check_sizes(S_total, D, rank);
   if (st != TSP_OK) return st;
-  if (B < 1) return fail(TSP_EINVAL, "B must be >= 1 (got %lld)", (long long)B);
-  if (Hq < 1 || Hkv < 1) return fail(TSP_EINVAL, "Hq and Hkv must be >= 1");
-  if (Hq % Hkv != 0) return fail(TSP_EINVAL, "Hq %lld not divisible by Hkv %lld", (long long)Hq, (long long)Hkv);
   if (dtype != TSP_BF16 && dtype != TSP_F32) return fail(TSP_EUNSUPPORTED, "unknown dtype %d", dtype);
   if (!kernel_shape(dtype, dh, ks)) return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
-  if (Hq > 65536 || B > 65536) return fail(TSP_EINVAL, "B or Hq too large");
-  // per-lane 32-bit byte offsets span one K/V stage: 64 keys of Hkv*dh elements
-  if (Hkv * dh > (int64_t(1) << 22)) return fail(TSP_EINVAL, "Hkv * dh above 2^22");
-
-  const int64_t C = S_total / (2 * D);
-  const int64_t grp = Hq / Hkv;
-  const int rows_per_wg = 32 * ks->waves * ks->row_blocks;
-  // Query heads per workgroup: the largest divisor of grp that also divides the
-  // workgroup's row blocks, so one K/V tile in LDS serves as many heads as possible.
-  int64_t GH = 1;
-  for (int64_t g = 1; g <= grp; ++g)
-    if (grp % g == 0 && (ks->waves * ks->row_blocks) % g == 0) GH = g;
-  const int64_t BQ = rows_per_wg / GH;
-  const int64_t n_qtiles = (2 * C + BQ - 1) / BQ;
-  const int64_t n_pairs = (n_qtiles + 1) / 2;
-  const int64_t n_units = B * Hkv * (grp / GH) * n_pairs;
-  if (n_units > 0x7fffffff) return fail(TSP_EINVAL, "problem too large for one launch");
-
-  p->S_total = (int32_t)S_total;
-  p->C = (int32_t)C;
-  p->S_local = (int32_t)(2 * C);
-  p->D = (int32_t)D;
-  p->rank = (int32_t)rank;
-  p->Hq = (int32_t)Hq;
-  p->Hkv = (int32_t)Hkv;
-  p->grp = (int32_t)grp;
-  p->GH = (int32_t)GH;
-  p->BQ = (int32_t)BQ;
-  p->n_qtiles = (int32_t)n_qtiles;
-  p->n_pairs = (int32_t)n_pairs;
-  p->n_hgroups = (int32_t)(grp / GH);
-  p->n_units = (int32_t)n_units;
-  p->scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
-  return TSP_OK;
+  return tsp_host::plan_tiles(B, S_total, D, rank, Hq, Hkv, dh, *ks, p);
 }
 
 template <int DH>
@@ -208,8 +149,7 @@ int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_fu
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TSP_ELAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
-  g_last_error[0] = '\0';
-  return TSP_OK;
+  return tsp_host::ok();
 }
 
 int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse, int64_t B,
@@ -250,8 +190,7 @@ int tsp_attn_merge(const void* out_a, const float* lse_a, const void* out_b, con
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TSP_ELAUNCH, "merge kernel launch failed: %s", hipGetErrorString(e));
-  g_last_error[0] = '\0';
-  return TSP_OK;
+  return tsp_host::ok();
 }
 
 int tsp_attn_zigzag_positions(int64_t S_total, int64_t D, int64_t rank, int64_t* out_host) {
@@ -323,6 +262,6 @@ const char* tsp_attn_strerror(int status) {
   }
 }
 
-const char* tsp_attn_last_error(void) { return g_last_error; }
+const char* tsp_attn_last_error(void) { return tsp_host::g_last_error; }
 
 }  // extern "C"

@@ -176,6 +176,42 @@ def test_merge_null_and_misaligned_pointers_rejected(lib):
         assert _merge_call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
 
 
+BWD_VALID = dict(B=1, S_total=512, D=4, rank=1, Hq=4, Hkv=1, dh=64, dtype=tsp.TSP_BF16)
+
+
+def _bwd_call(lib, ptrs=None, **kw):
+    a = dict(BWD_VALID)
+    a.update(kw)
+    p = ptrs if ptrs is not None else [_fake()] * 10
+    return lib.tsp_attn_bwd(*p, a["B"], a["S_total"], a["D"], a["rank"], a["Hq"], a["Hkv"], a["dh"], a["dtype"],
+                            None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=0), tsp.TSP_EINVAL),
+    (dict(rank=4), tsp.TSP_EINVAL),
+    (dict(S_total=500), tsp.TSP_EINVAL),
+    (dict(B=0), tsp.TSP_EINVAL),
+    (dict(Hq=6, Hkv=4), tsp.TSP_EINVAL),
+    (dict(Hq=65536, Hkv=1, dh=128), tsp.TSP_EINVAL),   # Hq * dh above 2^22
+    (dict(dh=96), tsp.TSP_EUNSUPPORTED),
+    (dict(dtype=tsp.TSP_F32), tsp.TSP_EUNSUPPORTED),
+    (dict(dtype=9), tsp.TSP_EUNSUPPORTED),
+])
+def test_bwd_invalid_arguments_rejected(lib, kw, code):
+    assert _bwd_call(lib, **kw) == code
+    assert lib.tsp_attn_last_error().decode() != ""
+
+
+def test_bwd_null_and_misaligned_pointers_rejected(lib):
+    for i in range(10):
+        ptrs = [_fake()] * 10
+        ptrs[i] = None
+        assert _bwd_call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
+        ptrs[i] = _fake(0x100008)
+        assert _bwd_call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
+
+
 def test_map_helpers_reject_bad_sizes(lib):
     assert lib.tsp_attn_unmasked_pairs(500, 4, 0) == tsp.TSP_EINVAL
     assert lib.tsp_attn_zigzag_positions(512, 4, 9, None) == tsp.TSP_EINVAL

@@ -92,3 +92,8 @@ def make_custom(B, S_total, D, Hq, Hkv, dh, dtype, seed):
     k = _randn((B, S_total, Hkv, dh), seed + 2, dtype)
     v = _randn((B, S_total, Hkv, dh), seed + 3, dtype)
     return q, k, v
+
+
+def make_grad(shape, seed: int, dtype) -> torch.Tensor:
+    """A seeded upstream gradient (N(0, 1), rounded like the inputs) for backward tests."""
+    return _randn(tuple(shape), seed, dtype)
