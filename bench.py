@@ -30,10 +30,14 @@ METRIC = "causal attention TFLOP/s per rank shard + % of bf16 MFMA peak (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
+# the sources of the forward kernel and of its launch configuration
+FORWARD_SOURCES = ("attn_common.h", "attn_fwd_bf16.h", "attn_fwd_f32.h", "zigzag.h", "tsp_attn.hip")
+
+
 def kernel_source_digest() -> str:
     csrc = os.path.join(ROOT, "sequence_causal_attention_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
+    for name in FORWARD_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -102,6 +106,9 @@ def main():
                     help="time the chunk-pipelined form instead: one key-range launch per gathered "
                          "chunk (2D of them, in ring arrival order), folded into the running result "
                          "in the kernel's epilogue (fused, the default) or by a separate merge launch")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward instead (tsp_attn_bwd: delta, dQ and dK/dV kernels) on the "
+                         "forward's out / lse; FLOPs counted as 5 products of 2*dh per visible pair")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run plain device copies of MIB MiB (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -144,7 +151,17 @@ def main():
     bounds = [(c * w.C, (c + 1) * w.C) for c in chunks]
     part_o, part_l = torch.empty_like(out), torch.empty_like(lse)
 
+    if args.backward:
+        tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream)
+        dout = workloads.make_grad(qd.shape, 99, qd.dtype).to(dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        delta = torch.empty_like(lse)
+        torch.cuda.synchronize()
+
     def step():
+        if args.backward:
+            tsp.bwd(qd, kd, vd, out, lse, dout, D=w.D, rank=rank, dq=dq, dk=dk, dv=dv, delta=delta, stream=stream)
+            return
         if not args.chunk_pipeline:
             tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream)
             return
@@ -173,14 +190,15 @@ def main():
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
 
-    flops = 4.0 * w.B * w.Hq * w.dh * w.C * (w.S_total + 1)
+    # causal FLOPs: 2 products (forward) or 5 (backward) of 2*dh per visible pair per query head
+    flops = (10.0 if args.backward else 4.0) * w.B * w.Hq * w.dh * w.C * (w.S_total + 1)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
 
     cpu = None
-    if not args.no_cpu_baseline and not args.chunk_pipeline:
+    if not args.no_cpu_baseline and not args.chunk_pipeline and not args.backward:
         cpu = cpu_baseline(w, rank, q, k, v, args.cpu_budget)
 
     line = {
@@ -201,7 +219,8 @@ def main():
             "workload": w.name, "B": w.B, "S_total": w.S_total, "D": w.D, "rank": rank, "Hq": w.Hq,
             "Hkv": w.Hkv, "dh": w.dh, "local_queries": w.S_local, "flops_per_step": flops,
             "parallelism": "one sequence-parallel rank's shard on 1 GPU",
-            "form": ("single launch" if not args.chunk_pipeline else
+            "form": ("backward: delta, dQ and dK/dV launches" if args.backward else
+                     "single launch" if not args.chunk_pipeline else
                      f"chunk pipeline: {len(bounds)} key-range launches, merged in the epilogue"
                      if args.chunk_pipeline == "fused" else
                      f"chunk pipeline: {len(bounds)} key-range launches + {len(bounds) - 1} merge launches"),
@@ -212,7 +231,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None if args.chunk_pipeline else measured_traffic(w.name, flops),
+            "traffic": None if (args.chunk_pipeline or args.backward) else measured_traffic(w.name, flops),
             "kernel_ms": round(kernel_ms, 4),
         },
         "cpu_baseline": cpu,

@@ -21,8 +21,11 @@ LIB = os.path.join(PKG, "libtsp_attn.so")
 UNITS = [
     # forward kernels: MFMA results in arch VGPRs, the score tiles feed the VALU softmax
     (os.path.join(CSRC, "tsp_attn.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
-    # backward kernels: the dK/dV accumulators live in the accumulation registers
-    (os.path.join(CSRC, "tsp_attn_bwd.hip"), []),
+    # backward kernels, dh 64 / 128: the same
+    (os.path.join(CSRC, "tsp_attn_bwd.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
+    # backward kernels, dh 256: the dK/dV accumulators fill the arch VGPRs, so MFMA
+    # results stay in the accumulation registers
+    (os.path.join(CSRC, "tsp_attn_bwd256.hip"), []),
 ]
 SOURCES = [u[0] for u in UNITS]
 HEADERS = [os.path.join(ROOT, "include", "tsp_attn.h")] + [

@@ -157,12 +157,14 @@ struct BwdQTile {
   static_assert((2 * WL) % NW == 0, "stage loads must split evenly over the waves");
 };
 
-template <int DH, int NW, int NBUF>
+// PIPE: issue the next step's S / dP products ahead of the current step's VALU work (one
+// more score tile live; off where the registers do not allow it).
+template <int DH, int NW, int NBUF, bool PIPE>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkv_bf16_kernel(TspBwdParams bp) {
   using T = BwdQTile<DH, NW>;
   constexpr int NDB = DH / 32, NKK = DH / 16, PD = NBUF - 1, KB = 32 * NW;
   constexpr int VM_STAGE = T::LPW + 1;  // loads per wave per stage (tiles + metadata)
-  static_assert(VM_STAGE * (PD - 1) < 64, "vmcnt range");
+  static_assert(PD >= 2 && VM_STAGE * (PD - 1) < 64, "ring depth / vmcnt range");
   const TspParams& p = bp.f;
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * T::STAGE_BYTES];
@@ -283,21 +285,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkv_bf16_kernel(TspBwdPar
     }
 
   const int32_t wave_key_max = j0 + 32 * wave + 31;
-#pragma unroll 1
-  for (int u = 0; u < PD; ++u) issue(u);
-#pragma unroll 1
-  for (int t = 0; t < n_steps; ++t) {
-    tsp_wait_vm<VM_STAGE * (PD - 1)>();  // stage t landed (this wave's part)
-    __syncthreads();                     // ... for every wave; the slot of t-1 is free
-    issue(t + PD);
 
+  // S = Q K^T and dP = dO V^T of step t: lane holds key `col`, query rows
+  // 8(e/4) + 4*half + e%4 of the step's tile
+  auto sdp = [&](int t, tsp_f32x16& s, tsp_f32x16& dp) {
     const uint8_t* qs = smem + (t % NBUF) * T::STAGE_BYTES;
     const uint8_t* ds = qs + T::TILE_BYTES;
-    const float* meta = reinterpret_cast<const float*>(qs + 2 * T::TILE_BYTES + wave * T::META_BYTES);
-    const int32_t i0 = (t_first + t % tiles) * 32;
-
-    // S = Q K^T and dP = dO V^T: lane holds key `col`, query rows 8(e/4) + 4*half + e%4
-    tsp_f32x16 s, dp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       s[e] = 0.f;
@@ -313,37 +306,55 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkv_bf16_kernel(TspBwdPar
       const tsp_bf16x8 da = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(ds + qoff[kk]));
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
     }
+  };
 
-    // P = exp2(s * log2(e)/sqrt(dh) - lse * log2(e)) on visible pairs, dS = P (dP - Delta)
+  // P = exp2(s * log2(e)/sqrt(dh) - lse * log2(e)) on visible pairs, dS = P (dP - Delta),
+  // then dV^T += dO^T P and dK^T += Q^T dS (rows = dims, columns = keys)
+  auto grads = [&](int t, const tsp_f32x16& s, const tsp_f32x16& dp) {
+    const uint8_t* qs = smem + (t % NBUF) * T::STAGE_BYTES;
+    const uint8_t* ds = qs + T::TILE_BYTES;
+    const float* meta = reinterpret_cast<const float*>(qs + 2 * T::TILE_BYTES + wave * T::META_BYTES);
+    const int32_t i0 = (t_first + t % tiles) * 32;
     const int32_t pos0 = tsp_zigzag_position(i0, C, p.D, p.rank);
     const bool irregular = i0 + 31 >= p.S_local || (i0 < C && i0 + 31 >= C);
-    const bool need_mask = irregular || wave_key_max > pos0;
-    float pw[16], dsw[16];
+    // exponent arguments of the lane's 16 rows
+    float x[16], del[16];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const tsp_f32x4 lse4 = *reinterpret_cast<const tsp_f32x4*>(meta + 8 * a + 4 * half);
       const tsp_f32x4 del4 = *reinterpret_cast<const tsp_f32x4*>(meta + 32 + 8 * a + 4 * half);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int v = 4 * a + e;
-        float pv = tsp_exp2(fmaf(s[v], p.scale_log2, -lse4[e] * TSP_LOG2E));
-        if (need_mask) {
-          const int32_t row = i0 + 8 * a + 4 * half + e;
-          const int32_t pos = irregular ? tsp_zigzag_position(min(row, p.S_local - 1), C, p.D, p.rank)
-                                        : pos0 + 8 * a + 4 * half + e;
-          if (row >= p.S_local || key > pos) pv = 0.f;
-        }
-        pw[v] = pv;
-        dsw[v] = pv * (dp[v] - del4[e]);
+        x[4 * a + e] = fmaf(s[4 * a + e], p.scale_log2, -lse4[e] * TSP_LOG2E);
+        del[4 * a + e] = del4[e];
       }
+    }
+    // causal mask (steps that reach past a row's position, and irregular tiles that hold
+    // a chunk boundary or rows past the last): masked arguments become -inf, weight 0
+    if (irregular) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int32_t row = i0 + 8 * (v >> 2) + 4 * half + (v & 3);
+        const int32_t pos = tsp_zigzag_position(min(row, p.S_local - 1), C, p.D, p.rank);
+        if (row >= p.S_local || key > pos) x[v] = -INFINITY;
+      }
+    } else if (wave_key_max > pos0) {
+      const int32_t lim = key - pos0 - 4 * half;  // row offsets below this see no key
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (8 * (v >> 2) + (v & 3) < lim) x[v] = -INFINITY;
+    }
+    float pw[16], dsw[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      pw[v] = tsp_exp2(x[v]);
+      dsw[v] = pw[v] * (dp[v] - del[v]);
     }
     tsp_bf16x8 pf[2], dsf[2];
     pf[0] = tsp_pack8(pw);
     pf[1] = tsp_pack8(pw + 8);
     dsf[0] = tsp_pack8(dsw);
     dsf[1] = tsp_pack8(dsw + 8);
-
-    // dV^T += dO^T P and dK^T += Q^T dS: rows = dims, columns = keys
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -354,6 +365,43 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkv_bf16_kernel(TspBwdPar
         const tsp_bf16x8 qT = tsp_tr_read8(qs + tlo[db] + ro, qs + thi[db] + ro);
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf[st], dk[db], 0, 0, 0);
       }
+  };
+
+  // Step t: the S / dP products of step t+1 go to the matrix pipe ahead of step t's VALU
+  // work, then step t's dV / dK products. Stages t and t+1 are read in step t, so the
+  // stage issued here, NBUF-1 ahead, takes the slot of stage t-1.
+  auto step = [&](int t, tsp_f32x16& sc, tsp_f32x16& dc, tsp_f32x16& sn, tsp_f32x16& dn) {
+    tsp_wait_vm<VM_STAGE * (PD - 2)>();  // stage t+1 landed (this wave's part)
+    __syncthreads();                     // ... for every wave; every wave is past step t-1
+    issue(t + PD);
+    sdp(t + 1, sn, dn);  // past the last step this reads a duplicate stage; unused
+    grads(t, sc, dc);
+  };
+
+#pragma unroll 1
+  for (int u = 0; u < PD; ++u) issue(u);
+  if constexpr (PIPE) {
+    tsp_wait_vm<VM_STAGE * (PD - 1)>();
+    __syncthreads();
+    tsp_f32x16 s0, d0, s1, d1;
+    sdp(0, s0, d0);
+    int t = 0;
+#pragma unroll 1
+    for (; t + 2 <= n_steps; t += 2) {
+      step(t, s0, d0, s1, d1);
+      step(t + 1, s1, d1, s0, d0);
+    }
+    if (t < n_steps) step(t, s0, d0, s1, d1);
+  } else {
+#pragma unroll 1
+    for (int t = 0; t < n_steps; ++t) {
+      tsp_wait_vm<VM_STAGE * (PD - 1)>();  // stage t landed (this wave's part)
+      __syncthreads();                     // ... for every wave; the slot of stage t-1 is free
+      issue(t + PD);
+      tsp_f32x16 s0, d0;
+      sdp(t, s0, d0);
+      grads(t, s0, d0);
+    }
   }
   tsp_wait_vm<0>();  // the trailing duplicate loads land before the workgroup ends
 

@@ -1,0 +1,31 @@
+// bwd_config.h -- tile configuration and launch entry of the backward kernels, shared by
+// the backward translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "attn_bwd_bf16.h"
+
+// Tile configuration per head dim: waves of the key-stationary and query-stationary
+// kernels, their LDS ring depths, and the query-stationary kernel's waves per SIMD.
+template <int DH>
+struct BwdCfg {
+  static constexpr int KV_NW = 4, KV_NBUF = 4;
+  static constexpr bool KV_PIPE = false;
+  static constexpr int Q_NW = 4, Q_NBUF = 4, Q_OCC = DH <= 128 ? 2 : 1;
+};
+
+// The kernels of one head dim, in the order delta, dQ, dK/dV. Instantiated for dh 64 and
+// 128 in tsp_attn_bwd.hip and for dh 256 in tsp_attn_bwd256.hip.
+template <int DH>
+void tsp_bwd_launch(const tsp::TspBwdParams& bp, int64_t kv_units, hipStream_t s) {
+  using C = BwdCfg<DH>;
+  const int64_t threads = bp.n_rows * (DH / 8);
+  hipLaunchKernelGGL((tsp::attn_bwd_delta_bf16_kernel<DH>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     s, bp);
+  hipLaunchKernelGGL((tsp::attn_bwd_dq_bf16_kernel<DH, C::Q_NW, C::Q_NBUF, C::Q_OCC>), dim3(bp.f.n_units),
+                     dim3(C::Q_NW * 64), 0, s, bp);
+  hipLaunchKernelGGL((tsp::attn_bwd_dkv_bf16_kernel<DH, C::KV_NW, C::KV_NBUF, C::KV_PIPE>), dim3((unsigned)kv_units),
+                     dim3(C::KV_NW * 64), 0, s, bp);
+}
+

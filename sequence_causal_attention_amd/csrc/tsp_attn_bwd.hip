@@ -1,13 +1,12 @@
 // tsp_attn_bwd.hip -- C ABI of the backward of the per-rank zigzag / GQA causal attention
 // (gfx950): argument validation, work decomposition and dispatch of the three backward
-// kernels (attn_bwd_bf16.h). Built as its own translation unit: the key-stationary
-// kernel keeps its dK/dV accumulators in the accumulation registers, so this file is
-// compiled without the flag that moves MFMA results into the arch VGPRs.
+// kernels (attn_bwd_bf16.h).
 #include <hip/hip_runtime.h>
 
 #include "tsp_attn.h"
 #include "attn_bwd_bf16.h"
 #include "host_common.h"
+#include "bwd_config.h"
 
 namespace {
 
@@ -15,25 +14,14 @@ using tsp_host::aligned16;
 using tsp_host::fail;
 using tsp_host::KernelShape;
 
-// Tile configuration per head dim: waves of the key-stationary and query-stationary
-// kernels, their LDS ring depths, and the query-stationary kernel's waves per SIMD.
-template <int DH>
-struct BwdCfg {
-  static constexpr int KV_NW = 4, KV_NBUF = 4;
-  static constexpr int Q_NW = 4, Q_NBUF = 4, Q_OCC = DH <= 128 ? 2 : 1;
-};
+}  // namespace
 
-template <int DH>
-void launch(const tsp::TspBwdParams& bp, int64_t kv_units, hipStream_t s) {
-  using C = BwdCfg<DH>;
-  const int64_t threads = bp.n_rows * (DH / 8);
-  hipLaunchKernelGGL((tsp::attn_bwd_delta_bf16_kernel<DH>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     s, bp);
-  hipLaunchKernelGGL((tsp::attn_bwd_dq_bf16_kernel<DH, C::Q_NW, C::Q_NBUF, C::Q_OCC>), dim3(bp.f.n_units),
-                     dim3(C::Q_NW * 64), 0, s, bp);
-  hipLaunchKernelGGL((tsp::attn_bwd_dkv_bf16_kernel<DH, C::KV_NW, C::KV_NBUF>), dim3((unsigned)kv_units),
-                     dim3(C::KV_NW * 64), 0, s, bp);
-}
+template void tsp_bwd_launch<64>(const tsp::TspBwdParams&, int64_t, hipStream_t);
+template void tsp_bwd_launch<128>(const tsp::TspBwdParams&, int64_t, hipStream_t);
+// dh 256 is instantiated in tsp_attn_bwd256.hip (built with other code-generation flags)
+extern template void tsp_bwd_launch<256>(const tsp::TspBwdParams&, int64_t, hipStream_t);
+
+namespace {
 
 template <int DH>
 int kv_block() {
@@ -88,9 +76,9 @@ int tsp_attn_bwd(const void* q_local, const void* k_full, const void* v_full, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   switch (dh) {
-    case 64: launch<64>(bp, kv_units, s); break;
-    case 128: launch<128>(bp, kv_units, s); break;
-    case 256: launch<256>(bp, kv_units, s); break;
+    case 64: tsp_bwd_launch<64>(bp, kv_units, s); break;
+    case 128: tsp_bwd_launch<128>(bp, kv_units, s); break;
+    case 256: tsp_bwd_launch<256>(bp, kv_units, s); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TSP_ELAUNCH, "backward kernel launch failed: %s", hipGetErrorString(e));
