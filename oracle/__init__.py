@@ -13,3 +13,4 @@ from .attention import (  # noqa: F401
     visible,
     zigzag_positions,
 )
+from . import ulysses  # noqa: F401,E402

@@ -3,8 +3,8 @@
 Each ``pin_*`` takes an oracle namespace ``o`` (attributes ``causal_attention``,
 ``causal_attention_bruteforce``, ``zigzag_positions``, ``unmasked_pairs``,
 ``kv_head_of``, ``causal_attention_range``, ``merge_partials``,
-``causal_attention_backward``) and raises AssertionError when the implementation breaks
-the pin. The
+``causal_attention_backward``, ``ulysses``) and raises AssertionError when the
+implementation breaks the pin. The
 same pins run against deliberately broken copies in test_oracle_mutants.py, which
 shows that a plausible mistake anywhere in the oracle trips at least one of them.
 """
@@ -404,6 +404,57 @@ def pin_bwd_gqa_and_subset(o):
     assert np.array_equal(sv, dv[:, :, 1:2])
 
 
+# -- the Ulysses layout changes ---------------------------------------------------------
+
+def _coded(shape):
+    """Every element holds its own index (a provenance code)."""
+    return np.arange(int(np.prod(shape)), dtype=np.int64).reshape(shape)
+
+
+def pin_ulysses_pack_elementwise(o):
+    """pack_heads / gather_sequence against element-by-element loops over every index."""
+    u = o.ulysses
+    B, S_local, P, Hl, dh = 2, 3, 4, 2, 3
+    x = _coded((B, S_local, P * Hl, dh))
+    send = u.pack_heads(x, P)
+    assert send.shape == (P, B, S_local, Hl, dh)
+    for r in range(P):
+        for b in range(B):
+            for s in range(S_local):
+                for hl in range(Hl):
+                    for d in range(dh):
+                        assert send[r, b, s, hl, d] == x[b, s, r * Hl + hl, d]
+    recv = _coded((P, B, S_local, Hl, dh))
+    full = u.gather_sequence(recv)
+    assert full.shape == (B, P * S_local, Hl, dh)
+    for p in range(P):
+        for b in range(B):
+            for s in range(S_local):
+                assert np.array_equal(full[b, p * S_local + s], recv[p, b, s])
+
+
+def pin_ulysses_round_trip_and_heads(o):
+    """Simulated P ranks: pack + all-to-all + gather gives rank r the whole sequence of its
+    contiguous heads (the head-subset definition, by slicing the unsharded tensor); the
+    reverse path (scatter + all-to-all + unpack) returns every rank its own tokens with
+    all heads. The lesson's example: 24 heads over degree 4 give 6 heads per rank."""
+    u = o.ulysses
+    assert list(u.heads_of_rank(24, 4, 1)) == list(range(6, 12))
+    for B, S, H, dh, P in [(1, 16, 8, 4, 4), (2, 12, 6, 2, 3), (1, 8, 4, 3, 1)]:
+        xf = _coded((B, S, H, dh))
+        S_local, Hl = S // P, H // P
+        shards = [xf[:, p * S_local:(p + 1) * S_local] for p in range(P)]
+        recvs = u.all_to_all([u.pack_heads(x, P) for x in shards])
+        fulls = [u.gather_sequence(rv) for rv in recvs]
+        for r in range(P):
+            assert np.array_equal(fulls[r], xf[:, :, r * Hl:(r + 1) * Hl]), (B, S, H, P, r)
+        back = u.all_to_all([u.scatter_sequence(f, P) for f in fulls])
+        for p in range(P):
+            assert np.array_equal(u.unpack_heads(back[p], P), shards[p])
+        for x in shards:
+            assert np.array_equal(u.unpack_heads(u.pack_heads(x, P), P), x)
+
+
 ALL_PINS = [
     pin_zigzag_golden,
     pin_zigzag_permutation,
@@ -426,4 +477,6 @@ ALL_PINS = [
     pin_bwd_rank_partition,
     pin_bwd_closed_forms,
     pin_bwd_gqa_and_subset,
+    pin_ulysses_pack_elementwise,
+    pin_ulysses_round_trip_and_heads,
 ]

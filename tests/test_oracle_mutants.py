@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as A
+import oracle.ulysses as U
 from pins import ALL_PINS
 
 
@@ -89,6 +90,7 @@ def _namespace():
               "unmasked_pairs", "kv_head_of", "causal_attention_range", "merge_partials",
               "causal_attention_backward"):
         setattr(ns, n, getattr(A, n))
+    ns.ulysses = U
     return ns
 
 
@@ -220,3 +222,33 @@ def test_backward_mutant_copy_is_faithful():
     ns = _namespace()
     ns.causal_attention_backward = _bwd_mutant("none")
     assert not [f for f in _failures(ns) if f.startswith("pin_bwd")]
+
+
+def _ulysses_mutant(kind):
+    """A copy of the oracle's Ulysses module with one plausible mistake."""
+    m = types.SimpleNamespace(**{n: getattr(U, n) for n in
+                                 ("heads_of_rank", "pack_heads", "unpack_heads", "gather_sequence",
+                                  "scatter_sequence", "all_to_all")})
+    if kind == "interleaved_heads":  # head h to rank h % P
+        def pack(x, P):
+            x = np.asarray(x)
+            return np.stack([x[:, :, r::P, :] for r in range(P)], axis=0)
+        m.pack_heads = pack
+    elif kind == "sequence_order_reversed":  # blocks stored in reverse source order
+        def gather(recv):
+            recv = np.asarray(recv)
+            return U.gather_sequence(recv[::-1])
+        m.gather_sequence = gather
+    elif kind == "pack_axes_swapped":  # [B, P, ...] instead of [P, B, ...]
+        def pack(x, P):
+            return np.swapaxes(U.pack_heads(x, P), 0, 1).reshape(U.pack_heads(x, P).shape)
+        m.pack_heads = pack
+    return m
+
+
+@pytest.mark.parametrize("kind", ["interleaved_heads", "sequence_order_reversed", "pack_axes_swapped"])
+def test_ulysses_mutant_is_caught(kind):
+    ns = _namespace()
+    ns.ulysses = _ulysses_mutant(kind)
+    failed = [f for f in _failures(ns) if f.startswith("pin_ulysses")]
+    assert failed, f"Ulysses mutant {kind} passed every Ulysses pin"
