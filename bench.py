@@ -93,6 +93,62 @@ def cpu_baseline(w, rank, q, k, v, budget_s: float):
     }
 
 
+def ulysses_bench(args, torch, tsp, workloads):
+    """The local permutes of Ulysses sequence parallelism for one of P ranks (HBM-bound)."""
+    name = args.workload if args.workload != "tsp_7b_shard_s32k" else "ulysses_head_subset_s128k"
+    w = workloads.BY_NAME[name]
+    P = args.ulysses
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S_local = w.S_total // P
+    shapes = {"q": (w.B, S_local, w.Hq * P, w.dh), "k": (w.B, S_local, w.Hkv * P, w.dh),
+              "v": (w.B, S_local, w.Hkv * P, w.dh)}
+    xs = {n: workloads.make_grad(s, 7 + i, torch.bfloat16).to(dev) for i, (n, s) in enumerate(shapes.items())}
+    sends = {n: torch.empty((P, w.B, S_local, s[2] // P, w.dh), dtype=torch.bfloat16, device=dev)
+             for n, s in shapes.items()}
+    fulls = {n: torch.empty((w.B, w.S_total, s[2] // P, w.dh), dtype=torch.bfloat16, device=dev)
+             for n, s in shapes.items()}
+    o_send = torch.empty_like(sends["q"])
+    o_back = torch.empty_like(xs["q"])
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for n in ("q", "k", "v"):
+            tsp.ulysses_pack_heads(xs[n], P, out=sends[n], stream=stream)
+            tsp.ulysses_gather_sequence(sends[n], out=fulls[n], stream=stream)  # (exchange elided)
+        tsp.ulysses_scatter_sequence(fulls["q"], P, out=o_send, stream=stream)  # attention output stand-in
+        tsp.ulysses_unpack_heads(o_send, out=o_back, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    moved = 2 * sum(2 * t.numel() * 2 for t in xs.values()) + 2 * 2 * o_back.numel() * 2  # read + write
+    ms = wall * 1e3 / args.steps
+    line = {
+        "metric": "Ulysses layout-change bandwidth per rank (1 GPU)", "value": round(moved / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "P": P, "S_local": S_local, "heads_before": shapes["q"][2],
+                   "heads_after": w.Hq, "dh": w.dh, "bytes_per_step": moved,
+                   "form": "pack + gather of q, k, v; scatter + unpack of the output (8 launches)"},
+        "roofline": {"bound": "hbm", "achieved": round(moved / (kernel_ms * 1e-3) / 1e9, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(moved / (kernel_ms * 1e-3) / 1e9 / 8000.0, 4), "traffic": None,
+                     "kernel_ms": round(kernel_ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +165,11 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward instead (tsp_attn_bwd: delta, dQ and dK/dV kernels) on the "
                          "forward's out / lse; FLOPs counted as 5 products of 2*dh per visible pair")
+    ap.add_argument("--ulysses", type=int, default=0, metavar="P",
+                    help="time the Ulysses layout changes of one of P ranks instead: head pack and "
+                         "sequence gather of q, k, v before the attention, sequence scatter and head "
+                         "unpack of its output after (the workload is the attention shape after the "
+                         "exchange); reports GB/s moved")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run plain device copies of MIB MiB (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -133,6 +194,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": max(1, args.steps)}), flush=True)
         return
+
+    if args.ulysses:
+        return ulysses_bench(args, torch, tsp, workloads)
 
     w = workloads.BY_NAME[args.workload]
     rank = w.ranks[0] if args.rank is None else args.rank

@@ -145,6 +145,38 @@ int tsp_attn_bwd(const void* q_local, const void* k_full, const void* v_full, co
                  int64_t Hkv, int64_t dh, int dtype, void* stream);
 
 /*
+ * Ulysses layout changes around the one-rank (D = 1) attention. DeepSpeed-Ulysses
+ * transposes between sequence partitions and head partitions with an all-to-all, so each
+ * of P ranks attends over the whole sequence for H/P heads, then transposes back
+ * ("Tensor, pipeline e sequence parallelism", section 01, sequence-parallel paragraph;
+ * "AutoSP ...", section 2.A items 2-3). Rank p holds the contiguous sequence chunk p of
+ * S_local tokens; heads are split contiguously (rank r: heads r*H/P .. (r+1)*H/P - 1).
+ * These are the local permutes on either side of the collective; the collective itself
+ * moves block r of a rank's send buffer to rank r, which stores it as block p (p = the
+ * sender), so the receive buffer is in sequence order.
+ *
+ *   tsp_ulysses_pack_heads      x [B, S_local, H, dh] -> send [P, B, S_local, H/P, dh]
+ *                               (send[r] = this rank's tokens, heads of rank r)
+ *   tsp_ulysses_unpack_heads    send [P, B, S_local, H/P, dh] -> x [B, S_local, H, dh]
+ *   tsp_ulysses_gather_sequence recv [P, B, S_local, Hl, dh] -> full [B, P*S_local, Hl, dh]
+ *                               (block p = sequence chunk p; the attention input)
+ *   tsp_ulysses_scatter_sequence full [B, P*S_local, Hl, dh] -> send [P, B, S_local, Hl, dh]
+ *
+ * Device buffers, contiguous, element type `dtype` (TSP_BF16 or TSP_F32; the data is only
+ * moved), 16-byte aligned, input and output not overlapping; dh * element size a multiple
+ * of 16; H divisible by P; at most 64 GiB per tensor. Enqueued on `stream`. Returns
+ * TSP_OK, TSP_EINVAL, TSP_EUNSUPPORTED or TSP_ELAUNCH. Results are bit-exact copies.
+ */
+int tsp_ulysses_pack_heads(const void* x, void* send, int64_t B, int64_t S_local, int64_t H,
+                           int64_t dh, int64_t P, int dtype, void* stream);
+int tsp_ulysses_unpack_heads(const void* send, void* x, int64_t B, int64_t S_local, int64_t H,
+                             int64_t dh, int64_t P, int dtype, void* stream);
+int tsp_ulysses_gather_sequence(const void* recv, void* full, int64_t B, int64_t S_local,
+                                int64_t Hl, int64_t dh, int64_t P, int dtype, void* stream);
+int tsp_ulysses_scatter_sequence(const void* full, void* send, int64_t B, int64_t S_local,
+                                 int64_t Hl, int64_t dh, int64_t P, int dtype, void* stream);
+
+/*
  * tsp_attn_zigzag_positions -- the zigzag map on the host: writes g(i) for the 2C local
  * rows of `rank` into out_host (caller-owned host memory of 2C int64).
  * ("Folding Tensor and Sequence Parallelism ...", section 2, zigzag partitioning.)

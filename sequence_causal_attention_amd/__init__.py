@@ -41,6 +41,10 @@ SIGNATURES = {
                                           _I64, _I64, ctypes.c_int, ctypes.c_int, _VP]),
     "tsp_attn_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "tsp_attn_bwd": (ctypes.c_int, [_VP] * 10 + [_I64] * 7 + [ctypes.c_int, _VP]),
+    "tsp_ulysses_pack_heads": (ctypes.c_int, [_VP, _VP] + [_I64] * 5 + [ctypes.c_int, _VP]),
+    "tsp_ulysses_unpack_heads": (ctypes.c_int, [_VP, _VP] + [_I64] * 5 + [ctypes.c_int, _VP]),
+    "tsp_ulysses_gather_sequence": (ctypes.c_int, [_VP, _VP] + [_I64] * 5 + [ctypes.c_int, _VP]),
+    "tsp_ulysses_scatter_sequence": (ctypes.c_int, [_VP, _VP] + [_I64] * 5 + [ctypes.c_int, _VP]),
     "tsp_attn_zigzag_positions": (ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(_I64)]),
     "tsp_attn_zigzag_positions_device": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP]),
     "tsp_attn_unmasked_pairs": (_I64, [_I64, _I64, _I64]),
@@ -207,6 +211,51 @@ def bwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, out: 
                                 delta.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, code, handle)
     _check(st)
     return dq, dk, dv, delta
+
+
+def _ulysses_call(fn, src: torch.Tensor, out_shape, B, S_local, H, dh, P, out=None, stream=None):
+    if not src.is_cuda or not src.is_contiguous():
+        raise TspAttnError(TSP_EINVAL, "input must be a contiguous GPU tensor")
+    code = _dtype_code(src)
+    out = torch.empty(out_shape, dtype=src.dtype, device=src.device) if out is None else out
+    if tuple(out.shape) != tuple(out_shape) or out.dtype != src.dtype or not out.is_contiguous():
+        raise TspAttnError(TSP_EINVAL, f"output must be contiguous {tuple(out_shape)} {src.dtype}")
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(src.device):
+        _check(fn(src.data_ptr(), out.data_ptr(), B, S_local, H, dh, P, code, handle))
+    return out
+
+
+def ulysses_pack_heads(x: torch.Tensor, P: int, out=None, stream=None) -> torch.Tensor:
+    """x [B, S_local, H, dh] -> send [P, B, S_local, H/P, dh] (block r goes to rank r)."""
+    B, S_local, H, dh = x.shape
+    return _ulysses_call(lib().tsp_ulysses_pack_heads, x, (P, B, S_local, H // max(P, 1), dh), B, S_local, H, dh,
+                         P, out, stream)
+
+
+def ulysses_unpack_heads(send: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """send [P, B, S_local, H/P, dh] -> x [B, S_local, H, dh]."""
+    P, B, S_local, Hl, dh = send.shape
+    return _ulysses_call(lib().tsp_ulysses_unpack_heads, send, (B, S_local, Hl * P, dh), B, S_local, Hl * P, dh, P,
+                         out, stream)
+
+
+def ulysses_gather_sequence(recv: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """recv [P, B, S_local, Hl, dh] (block p = sequence chunk p) -> [B, P*S_local, Hl, dh]."""
+    P, B, S_local, Hl, dh = recv.shape
+    return _ulysses_call(lib().tsp_ulysses_gather_sequence, recv, (B, P * S_local, Hl, dh), B, S_local, Hl, dh, P,
+                         out, stream)
+
+
+def ulysses_scatter_sequence(full: torch.Tensor, P: int, out=None, stream=None) -> torch.Tensor:
+    """full [B, S, Hl, dh] -> send [P, B, S/P, Hl, dh] (block p goes back to rank p)."""
+    B, S, Hl, dh = full.shape
+    if P < 1 or S % P != 0:
+        raise TspAttnError(TSP_EINVAL, "sequence length must be divisible by P")
+    return _ulysses_call(lib().tsp_ulysses_scatter_sequence, full, (P, B, S // P, Hl, dh), B, S // P, Hl, dh, P,
+                         out, stream)
 
 
 def fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, S_total, D, rank, Hq, Hkv, dh, dtype, stream) -> int:

@@ -10,6 +10,7 @@
 #include "attn_fwd_bf16.h"
 #include "attn_fwd_f32.h"
 #include "attn_merge.h"
+#include "ulysses_permute.h"
 #include "host_common.h"
 
 namespace tsp_host {
@@ -99,6 +100,41 @@ void launch_bf16(const TspParams& p, hipStream_t stream) {
 template <int DH>
 void launch_f32(const TspParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((tsp::attn_fwd_f32_kernel<DH>), dim3(p.n_units), dim3(256), 0, stream, p);
+}
+
+// Validates a Ulysses layout change and launches the block transpose of [M][N] blocks.
+int ulysses_transpose(const char* what, const void* in, void* out, int64_t B, int64_t S_local, int64_t H,
+                      int64_t dh, int64_t P, int dtype, bool heads, bool forward, void* stream) {
+  if (!in || !out) return fail(TSP_EINVAL, "%s: null pointer argument", what);
+  if (!aligned16(in) || !aligned16(out)) return fail(TSP_EINVAL, "%s: pointers must be 16-byte aligned", what);
+  if (B < 1 || S_local < 1 || H < 1 || dh < 1 || P < 1)
+    return fail(TSP_EINVAL, "%s: B, S_local, heads, dh and P must be >= 1", what);
+  if (dtype != TSP_BF16 && dtype != TSP_F32) return fail(TSP_EUNSUPPORTED, "%s: unknown dtype %d", what, dtype);
+  const int64_t eb = dtype == TSP_BF16 ? 2 : 4;
+  if ((dh * eb) % 16 != 0) return fail(TSP_EUNSUPPORTED, "%s: dh * element size must be a multiple of 16", what);
+  if (heads && H % P != 0) return fail(TSP_EINVAL, "%s: H %lld not divisible by P %lld", what, (long long)H, (long long)P);
+  // heads: H is the total head count; sequence: H is the heads per rank
+  const int64_t hl = heads ? H / P : H;
+  const int64_t blk = heads ? hl * dh * eb : S_local * hl * dh * eb;
+  const int64_t outer = heads ? B * S_local : B;  // the index that stays with the tokens
+  const int64_t total = outer * P * (blk / 16);
+  if (total >= (int64_t(1) << 32)) return fail(TSP_EINVAL, "%s: tensor above 64 GiB", what);
+  tsp::BlockTransposeParams bp{};
+  bp.in = static_cast<const tsp_u32x4*>(in);
+  bp.out = static_cast<tsp_u32x4*>(out);
+  // pack heads / scatter sequence: [outer][P] -> [P][outer]; the inverses: [P][outer] -> [outer][P]
+  const bool to_rank_major = heads ? forward : !forward;
+  bp.M = (uint32_t)(to_rank_major ? outer : P);
+  bp.N = (uint32_t)(to_rank_major ? P : outer);
+  bp.cpb = (uint32_t)(blk / 16);
+  bp.total = (uint32_t)total;
+  const int64_t per_wg = 256 * tsp::TSP_PERMUTE_UNROLL;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(tsp::block_transpose_kernel, dim3((unsigned)((total + per_wg - 1) / per_wg)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), bp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TSP_ELAUNCH, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+  return tsp_host::ok();
 }
 
 __global__ void zigzag_dump_kernel(int32_t* out, int32_t n, int32_t C, int32_t D, int32_t rank) {
@@ -191,6 +227,26 @@ int tsp_attn_merge(const void* out_a, const float* lse_a, const void* out_b, con
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TSP_ELAUNCH, "merge kernel launch failed: %s", hipGetErrorString(e));
   return tsp_host::ok();
+}
+
+int tsp_ulysses_pack_heads(const void* x, void* send, int64_t B, int64_t S_local, int64_t H, int64_t dh, int64_t P,
+                           int dtype, void* stream) {
+  return ulysses_transpose("pack_heads", x, send, B, S_local, H, dh, P, dtype, true, true, stream);
+}
+
+int tsp_ulysses_unpack_heads(const void* send, void* x, int64_t B, int64_t S_local, int64_t H, int64_t dh,
+                             int64_t P, int dtype, void* stream) {
+  return ulysses_transpose("unpack_heads", send, x, B, S_local, H, dh, P, dtype, true, false, stream);
+}
+
+int tsp_ulysses_gather_sequence(const void* recv, void* full, int64_t B, int64_t S_local, int64_t Hl, int64_t dh,
+                                int64_t P, int dtype, void* stream) {
+  return ulysses_transpose("gather_sequence", recv, full, B, S_local, Hl, dh, P, dtype, false, true, stream);
+}
+
+int tsp_ulysses_scatter_sequence(const void* full, void* send, int64_t B, int64_t S_local, int64_t Hl, int64_t dh,
+                                 int64_t P, int dtype, void* stream) {
+  return ulysses_transpose("scatter_sequence", full, send, B, S_local, Hl, dh, P, dtype, false, false, stream);
 }
 
 int tsp_attn_zigzag_positions(int64_t S_total, int64_t D, int64_t rank, int64_t* out_host) {

@@ -22,7 +22,7 @@ HEADER = os.path.join(ROOT, "include", "tsp_attn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tsp_attn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tsp_(?:attn|ulysses)_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -210,6 +210,31 @@ def test_bwd_null_and_misaligned_pointers_rejected(lib):
         assert _bwd_call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
         ptrs[i] = _fake(0x100008)
         assert _bwd_call(lib, ptrs=ptrs) == tsp.TSP_EINVAL
+
+
+ULYSSES = ["tsp_ulysses_pack_heads", "tsp_ulysses_unpack_heads", "tsp_ulysses_gather_sequence",
+           "tsp_ulysses_scatter_sequence"]
+
+
+@pytest.mark.parametrize("fn", ULYSSES)
+@pytest.mark.parametrize("args,code", [
+    ((0, 16, 8, 128, 4, tsp.TSP_BF16), tsp.TSP_EINVAL),      # B = 0
+    ((1, 0, 8, 128, 4, tsp.TSP_BF16), tsp.TSP_EINVAL),       # S_local = 0
+    ((1, 16, 8, 128, 0, tsp.TSP_BF16), tsp.TSP_EINVAL),      # P = 0
+    ((1, 16, 8, 4, 4, tsp.TSP_BF16), tsp.TSP_EUNSUPPORTED),  # 8-byte rows
+    ((1, 16, 8, 128, 4, 7), tsp.TSP_EUNSUPPORTED),           # dtype
+])
+def test_ulysses_invalid_arguments_rejected(lib, fn, args, code):
+    f = _fake()
+    assert getattr(lib, fn)(f, f, *args, None) == code
+    assert getattr(lib, fn)(None, f, 1, 16, 8, 128, 4, tsp.TSP_BF16, None) == tsp.TSP_EINVAL
+    assert getattr(lib, fn)(f, _fake(0x100008), 1, 16, 8, 128, 4, tsp.TSP_BF16, None) == tsp.TSP_EINVAL
+
+
+def test_ulysses_heads_must_divide(lib):
+    f = _fake()
+    assert lib.tsp_ulysses_pack_heads(f, f, 1, 16, 6, 128, 4, tsp.TSP_BF16, None) == tsp.TSP_EINVAL
+    assert lib.tsp_ulysses_unpack_heads(f, f, 1, 16, 6, 128, 4, tsp.TSP_BF16, None) == tsp.TSP_EINVAL
 
 
 def test_map_helpers_reject_bad_sizes(lib):
