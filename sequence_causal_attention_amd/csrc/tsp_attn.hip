@@ -128,7 +128,7 @@ int ulysses_transpose(const char* what, const void* in, void* out, int64_t B, in
   bp.N = (uint32_t)(to_rank_major ? P : outer);
   bp.cpb = (uint32_t)(blk / 16);
   bp.total = (uint32_t)total;
-  const int64_t per_wg = 256 * tsp::TSP_PERMUTE_UNROLL;
+  const int64_t per_wg = 256 * tsp::TSP_PERMUTE_U;
   (void)hipGetLastError();
   hipLaunchKernelGGL(tsp::block_transpose_kernel, dim3((unsigned)((total + per_wg - 1) / per_wg)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), bp);

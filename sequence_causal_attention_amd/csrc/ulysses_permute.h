@@ -32,10 +32,16 @@ struct BlockTransposeParams {
   uint32_t total;     // M * N * cpb chunks
 };
 
-constexpr int TSP_PERMUTE_UNROLL = 4;
+#ifndef TSP_PERMUTE_UNROLL
+#define TSP_PERMUTE_UNROLL 2
+#endif
+#ifndef TSP_PERMUTE_NT
+#define TSP_PERMUTE_NT 0
+#endif
+constexpr int TSP_PERMUTE_U = TSP_PERMUTE_UNROLL;
 
 __global__ __launch_bounds__(256) void block_transpose_kernel(BlockTransposeParams p) {
-  constexpr int U = TSP_PERMUTE_UNROLL;
+  constexpr int U = TSP_PERMUTE_U;
   const uint32_t base = blockIdx.x * (256u * U) + threadIdx.x;
   tsp_u32x4 v[U];
 #pragma unroll
@@ -50,7 +56,13 @@ __global__ __launch_bounds__(256) void block_transpose_kernel(BlockTransposePara
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t idx = base + 256u * u;
-    if (idx < p.total) p.out[idx] = v[u];
+    if (idx < p.total) {
+#if TSP_PERMUTE_NT
+      __builtin_nontemporal_store(v[u], p.out + idx);  // streamed: not re-read by this kernel
+#else
+      p.out[idx] = v[u];
+#endif
+    }
   }
 }
 
