@@ -212,6 +212,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     dma_slot[q] = (isv ? St::TILE_BYTES : 0) + j * 1024;
   }
   const uint32_t smem_addr = __builtin_amdgcn_readfirstlane(tsp_lds_addr(smem));
+  const float inv_scale_log2 = 1.0f / p.scale_log2;
 
   for (int which = 0; which < 2; ++which) {
     const int32_t qt = which == 0 ? p.n_qtiles - 1 - pair : pair;
@@ -273,9 +274,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
 
     tsp_f32x16 acc[RB][NDB];
     float m_run[RB], l_run[RB];
+    float m_thr[RB];  // a score above this (raw units) needs a higher running max
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       m_run[rb] = -INFINITY;
+      m_thr[rb] = -INFINITY;
       l_run[rb] = 0.f;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -353,19 +356,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       }
     };
     auto needs_mask = [&](int s) { return s >= t_mask || s < u_left; };
+    // Row max of a step's scores over this lane's 16 keys (raw score units): the two
+    // halves of a row are tested separately, which decides the same wave-wide ballot as
+    // testing the full row, and the full max is formed only when a rescale is due.
     auto rowmax = [&](const tsp_f32x16(&sc)[RB], float(&mx)[RB]) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         float m = sc[rb][0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) m = fmaxf(m, sc[rb][e]);
-        mx[rb] = tsp_max_halves(m) * p.scale_log2;
+        mx[rb] = m;
       }
     };
     auto rescale_needed = [&](const float(&mx)[RB]) {
       bool need = false;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) need |= mx[rb] > m_run[rb] + TSP_RESCALE_SLACK;
+      for (int rb = 0; rb < RB; ++rb) need |= mx[rb] > m_thr[rb];
       return __builtin_amdgcn_ballot_w64(need) != 0;  // wave-uniform
     };
     // Raise the running max to cover this step (rare after the first step): scale the
@@ -373,7 +379,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     auto rescale = [&](const float(&mx)[RB]) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float m_new = fmaxf(m_run[rb], mx[rb]);
+        const float m_new = fmaxf(m_run[rb], tsp_max_halves(mx[rb]) * p.scale_log2);
+        m_thr[rb] = (m_new + TSP_RESCALE_SLACK) * inv_scale_log2;
         // a row with no visible key yet (both -inf) keeps its zero state
         const float alpha = m_new == -INFINITY ? 1.f : tsp_exp2(m_run[rb] - m_new);
         m_run[rb] = m_new;
