@@ -49,6 +49,12 @@
 #ifndef TSP_QK_SPLIT
 #define TSP_QK_SPLIT 0
 #endif
+#ifndef TSP_PINGPONG
+#define TSP_PINGPONG 1
+#endif
+#ifndef TSP_PP_LAGGED
+#define TSP_PP_LAGGED(w) ((w) >= NW / 2)
+#endif
 
 namespace tsp {
 
@@ -456,21 +462,31 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     const int32_t n_full = kv_end / St::BKS;  // stages with every key below kv_end
     const int t_fast = u_left == 0 ? min(t_mask - 1, (n_full - PD) * SPS - 1) : 0;
     tsp_f32x16 s_alt[RB];
-    auto fast_step = [&](auto u_const, int t0) {
+    // Stage boundary: wait until stage NEXT (relative to t0 / SPS) landed for every wave,
+    // then issue the stage PD ahead into the slot two stages back.
+    auto boundary = [&](auto next_const, int t0) {
+      constexpr int NEXT = decltype(next_const)::value;
+      __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // that stage landed (this wave's part)
+      __syncthreads();  // ... for every wave; the slot two stages back is free again
+      const int64_t adv = (int64_t)(t0 / SPS + NEXT + PD) * stage_stride;
+      const uint32_t base = smem_addr + ((NEXT + PD) % NBUF) * St::STAGE_BYTES;
+#pragma unroll
+      for (int q = 0; q < St::LPW; ++q)
+        tsp_lds_dma16((dma_isv[q] ? vbase : kbase) + adv, dma_voff[q], base + dma_slot[q]);
+    };
+    // LAG (second half of the waves, one of the two waves of each SIMD): the barrier of
+    // stage k comes after the PV products of step SPS*k - 2 instead of before the QK
+    // products of step SPS*k - 1. Every barrier still precedes the first read of its stage
+    // and follows the last read of the stage two back, but the two waves of a SIMD then run
+    // their matrix and vector phases in alternation (one's softmax under the other's MFMAs).
+    auto fast_step = [&](auto u_const, auto lag_const, int t0) {
       constexpr int U = decltype(u_const)::value;  // step t = t0 + U, t0 a multiple of GROUP
+      constexpr bool LAG = decltype(lag_const)::value;
       tsp_f32x16(&sc)[RB] = (U % 2 == 0) ? s_cur : s_alt;
       tsp_f32x16(&sn)[RB] = (U % 2 == 0) ? s_alt : s_cur;
       if (rescale_needed(mx)) rescale(mx);
-      if constexpr ((U + 1) % SPS == 0) {  // step t+1 opens a new stage
-        __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // that stage landed (this wave's part)
-        __syncthreads();  // ... for every wave; the slot two stages back is free again
-        constexpr int NEXT = (U + 1) / SPS;  // stage of step t+1, relative to t0 / SPS
-        const int64_t adv = (int64_t)(t0 / SPS + NEXT + PD) * stage_stride;
-        const uint32_t base = smem_addr + ((NEXT + PD) % NBUF) * St::STAGE_BYTES;
-#pragma unroll
-        for (int q = 0; q < St::LPW; ++q)
-          tsp_lds_dma16((dma_isv[q] ? vbase : kbase) + adv, dma_voff[q], base + dma_slot[q]);
-      }
+      if constexpr (!LAG && (U + 1) % SPS == 0)  // step t+1 opens a new stage
+        boundary(std::integral_constant<int, (U + 1) / SPS>{}, t0);
       tsp_bf16x8 pf[RB][2];
 #if TSP_SETPRIO
       __builtin_amdgcn_s_setprio(1);
@@ -487,6 +503,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
 #if TSP_SETPRIO
       __builtin_amdgcn_s_setprio(0);
 #endif
+      if constexpr (LAG && (U + 2) % SPS == 0)  // the next stage's barrier, one phase early
+        boundary(std::integral_constant<int, (U + 2) / SPS>{}, t0);
       rowmax(sn, mx);    // vector pipe: next step's row max
 #if TSP_SCHED == 1
       // issue order: all operand reads, then QK MFMAs each followed by a slice of the
@@ -514,11 +532,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       }
 #endif
     };
-    auto fast_group = [&]<int... Us>(std::integer_sequence<int, Us...>, int t0) {
-      (fast_step(std::integral_constant<int, Us>{}, t0), ...);
+    auto fast_group = [&]<int... Us>(std::integer_sequence<int, Us...>, auto lag_const, int t0) {
+      (fast_step(std::integral_constant<int, Us>{}, lag_const, t0), ...);
     };
     int t = 0;
-    for (; t + GROUP <= t_fast; t += GROUP) fast_group(std::make_integer_sequence<int, GROUP>{}, t);
+    constexpr bool PINGPONG = TSP_PINGPONG && SPS == 2 && NW % 2 == 0;
+    if (PINGPONG && TSP_PP_LAGGED(wave)) {
+      for (; t + GROUP <= t_fast; t += GROUP)
+        fast_group(std::make_integer_sequence<int, GROUP>{}, std::bool_constant<PINGPONG>{}, t);
+    } else {
+      for (; t + GROUP <= t_fast; t += GROUP)
+        fast_group(std::make_integer_sequence<int, GROUP>{}, std::false_type{}, t);
+    }
     int issued = t > 0 ? t / SPS + PD : pro;  // last stage issued so far
 
     // General path: the masked steps near the diagonal, the partial last stage and the

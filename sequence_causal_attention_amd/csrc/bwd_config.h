@@ -8,11 +8,20 @@
 
 // Tile configuration per head dim: waves of the key-stationary and query-stationary
 // kernels, their LDS ring depths, and the query-stationary kernel's waves per SIMD.
+#ifndef TSP_BWD_KV_NBUF
+#define TSP_BWD_KV_NBUF 4
+#endif
+#ifndef TSP_BWD_KV_PIPE
+#define TSP_BWD_KV_PIPE 0
+#endif
+#ifndef TSP_BWD_Q_NW
+#define TSP_BWD_Q_NW 4
+#endif
 template <int DH>
 struct BwdCfg {
-  static constexpr int KV_NW = 4, KV_NBUF = 4;
-  static constexpr bool KV_PIPE = false;
-  static constexpr int Q_NW = 4, Q_NBUF = 4, Q_OCC = DH <= 128 ? 2 : 1;
+  static constexpr int KV_NW = 4, KV_NBUF = DH <= 128 ? TSP_BWD_KV_NBUF : 4;
+  static constexpr bool KV_PIPE = DH <= 128 && TSP_BWD_KV_PIPE;
+  static constexpr int Q_NW = DH <= 128 ? TSP_BWD_Q_NW : 4, Q_NBUF = 4, Q_OCC = DH <= 128 ? 2 : 1;
 };
 
 // The kernels of one head dim, in the order delta, dQ, dK/dV. Instantiated for dh 64 and
