@@ -179,7 +179,7 @@ def bwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, out: 
         dout: torch.Tensor, *, D: int, rank: int, dq=None, dk=None, dv=None, delta=None, stream=None):
     """Backward of ``fwd`` (tsp_attn_bwd): returns (dq [B, 2C, Hq, dh], dk, dv
     [B, S_total, Hkv, dh] -- this rank's partial K/V gradients -- and delta [B, Hq, 2C]).
-    Outputs may be passed in preallocated. bf16 only."""
+    Outputs may be passed in preallocated. bf16 or fp32."""
     ins = (("q_local", q_local), ("k_full", k_full), ("v_full", v_full), ("out", out), ("dout", dout))
     for name, t in ins + (("lse", lse),):
         if not t.is_cuda or not t.is_contiguous():

@@ -47,6 +47,7 @@ struct TspBwdParams {
   void* dv;             // [B, S_total, Hkv, dh]
   float* delta;         // [B, Hq, S_local]
   int64_t n_rows;       // B * S_local * Hq
+  int64_t n_kv_rows;    // B * S_total * Hkv
   int32_t kv_need;      // (2D - rank) * C: keys that some local row sees
   int32_t n_kblocks;    // key blocks of the dK/dV kernel per (b, KV head)
   float scale;          // 1 / sqrt(dh)

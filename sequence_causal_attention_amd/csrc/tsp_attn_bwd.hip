@@ -7,6 +7,7 @@
 #include "attn_bwd_bf16.h"
 #include "host_common.h"
 #include "bwd_config.h"
+#include "attn_bwd_f32.h"
 
 namespace {
 
@@ -22,6 +23,16 @@ template void tsp_bwd_launch<128>(const tsp::TspBwdParams&, int64_t, hipStream_t
 extern template void tsp_bwd_launch<256>(const tsp::TspBwdParams&, int64_t, hipStream_t);
 
 namespace {
+
+template <int DH>
+void launch_f32(const tsp::TspBwdParams& bp, hipStream_t s) {
+  const int64_t threads = bp.n_rows * (DH / 4);
+  hipLaunchKernelGGL((tsp::attn_bwd_delta_f32_kernel<DH>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     bp);
+  hipLaunchKernelGGL((tsp::attn_bwd_dq_f32_kernel<DH>), dim3((unsigned)((bp.n_rows + 3) / 4)), dim3(256), 0, s, bp);
+  hipLaunchKernelGGL((tsp::attn_bwd_dkv_f32_kernel<DH>), dim3((unsigned)((bp.n_kv_rows + 3) / 4)), dim3(256), 0, s,
+                     bp);
+}
 
 template <int DH>
 int kv_block() {
@@ -43,8 +54,7 @@ int tsp_attn_bwd(const void* q_local, const void* k_full, const void* v_full, co
   }
   int st = tsp_host::check_sizes(S_total, D, rank);
   if (st != TSP_OK) return st;
-  if (dtype != TSP_BF16)
-    return fail(TSP_EUNSUPPORTED, dtype == TSP_F32 ? "the backward takes bf16 only" : "unknown dtype %d", dtype);
+  if (dtype != TSP_BF16 && dtype != TSP_F32) return fail(TSP_EUNSUPPORTED, "unknown dtype %d", dtype);
   if (dh != 64 && dh != 128 && dh != 256)
     return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
   if (Hq >= 1 && Hq * dh > (int64_t(1) << 22)) return fail(TSP_EINVAL, "Hq * dh above 2^22");
@@ -69,16 +79,27 @@ int tsp_attn_bwd(const void* q_local, const void* k_full, const void* v_full, co
   bp.dv = dv_full;
   bp.delta = delta;
   bp.n_rows = B * (int64_t)bp.f.S_local * Hq;
+  bp.n_kv_rows = B * S_total * Hkv;
+  if (dtype == TSP_F32 && (bp.n_rows > (int64_t(1) << 33) || bp.n_kv_rows > (int64_t(1) << 33)))
+    return fail(TSP_EINVAL, "problem too large for the fp32 backward");
   bp.kv_need = (int32_t)((2 * D - rank) * bp.f.C);
   bp.n_kblocks = (int32_t)n_kblocks;
   bp.scale = (float)(1.0 / std::sqrt((double)dh));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  switch (dh) {
-    case 64: tsp_bwd_launch<64>(bp, kv_units, s); break;
-    case 128: tsp_bwd_launch<128>(bp, kv_units, s); break;
-    case 256: tsp_bwd_launch<256>(bp, kv_units, s); break;
+  if (dtype == TSP_F32) {
+    switch (dh) {
+      case 64: launch_f32<64>(bp, s); break;
+      case 128: launch_f32<128>(bp, s); break;
+      case 256: launch_f32<256>(bp, s); break;
+    }
+  } else {
+    switch (dh) {
+      case 64: tsp_bwd_launch<64>(bp, kv_units, s); break;
+      case 128: tsp_bwd_launch<128>(bp, kv_units, s); break;
+      case 256: tsp_bwd_launch<256>(bp, kv_units, s); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TSP_ELAUNCH, "backward kernel launch failed: %s", hipGetErrorString(e));

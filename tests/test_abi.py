@@ -195,7 +195,6 @@ def _bwd_call(lib, ptrs=None, **kw):
     (dict(Hq=6, Hkv=4), tsp.TSP_EINVAL),
     (dict(Hq=65536, Hkv=1, dh=128), tsp.TSP_EINVAL),   # Hq * dh above 2^22
     (dict(dh=96), tsp.TSP_EUNSUPPORTED),
-    (dict(dtype=tsp.TSP_F32), tsp.TSP_EUNSUPPORTED),
     (dict(dtype=9), tsp.TSP_EUNSUPPORTED),
 ])
 def test_bwd_invalid_arguments_rejected(lib, kw, code):
