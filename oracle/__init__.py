@@ -14,3 +14,4 @@ from .attention import (  # noqa: F401
     zigzag_positions,
 )
 from . import ulysses  # noqa: F401,E402
+from . import tsp_layer  # noqa: F401,E402

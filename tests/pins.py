@@ -3,7 +3,7 @@
 Each ``pin_*`` takes an oracle namespace ``o`` (attributes ``causal_attention``,
 ``causal_attention_bruteforce``, ``zigzag_positions``, ``unmasked_pairs``,
 ``kv_head_of``, ``causal_attention_range``, ``merge_partials``,
-``causal_attention_backward``, ``ulysses``) and raises AssertionError when the
+``causal_attention_backward``, ``ulysses``, ``tsp_layer``) and raises AssertionError when the
 implementation breaks the pin. The
 same pins run against deliberately broken copies in test_oracle_mutants.py, which
 shows that a plausible mistake anywhere in the oracle trips at least one of them.
@@ -455,6 +455,65 @@ def pin_ulysses_round_trip_and_heads(o):
             assert np.array_equal(u.unpack_heads(u.pack_heads(x, P), P), x)
 
 
+# -- one rank's TSP attention layer ---------------------------------------------------
+
+def _layer_inputs(B, S, D, Hq, Hkv, dh, dm, seed):
+    xf = _rand((B, S, dm), seed) / np.sqrt(dm)
+    w_qkv = _rand(((Hq + 2 * Hkv) * dh, dm), seed + 1)
+    w_o = _rand((dm, Hq * dh), seed + 2) / np.sqrt(Hq * dh)
+    return xf, w_qkv, w_o
+
+
+def pin_layer_unsharded(o):
+    """Every rank's layer output equals the rows, at its zigzag positions, of the standard
+    causal multi-head attention layer on the whole sequence (computed here with PyTorch's
+    causal SDPA in fp64), when the gathered K/V hold the other ranks' projections; the
+    gathered buffers come back with all of the sequence's projections."""
+    for B, S, D, Hq, Hkv, dh, dm, seed in [(1, 32, 4, 4, 2, 8, 16, 90), (2, 24, 2, 6, 2, 4, 12, 91)]:
+        xf, w_qkv, w_o = _layer_inputs(B, S, D, Hq, Hkv, dh, dm, seed)
+        kf = (xf @ w_qkv[Hq * dh:(Hq + Hkv) * dh].T).reshape(B, S, Hkv, dh)
+        vf = (xf @ w_qkv[(Hq + Hkv) * dh:].T).reshape(B, S, Hkv, dh)
+        qf = (xf @ w_qkv[:Hq * dh].T).reshape(B, S, Hq, dh)
+        grp = Hq // Hkv
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qf).permute(0, 2, 1, 3),
+            torch.from_numpy(kf).permute(0, 2, 1, 3).repeat_interleave(grp, dim=1),
+            torch.from_numpy(vf).permute(0, 2, 1, 3).repeat_interleave(grp, dim=1), is_causal=True)
+        yf = ref.permute(0, 2, 1, 3).reshape(B, S, Hq * dh).numpy() @ w_o.T
+        for r in range(D):
+            pos = np.asarray(o.zigzag_positions(S, D, r))
+            garbage_k = np.where(np.isin(np.arange(S), pos)[None, :, None, None], 123.0, kf)
+            garbage_v = np.where(np.isin(np.arange(S), pos)[None, :, None, None], -7.0, vf)
+            y, K, V = o.tsp_layer.attention_layer(xf[:, pos], w_qkv, w_o, garbage_k, garbage_v, D, r, Hq, Hkv, dh)
+            assert np.allclose(y, yf[:, pos], rtol=0, atol=1e-10), (B, S, D, r)
+            assert np.allclose(K, kf, rtol=0, atol=1e-12) and np.allclose(V, vf, rtol=0, atol=1e-12)
+
+
+def pin_layer_shard_sum(o):
+    """The shard schedule: the layer with all heads equals the sum of the layers restricted
+    to each weight shard's heads (query heads i*Hq/D.., KV heads i*Hkv/D.., the matching
+    columns of W_O), which is what accumulating the output projection shard by shard adds up."""
+    B, S, D, Hq, Hkv, dh, dm = 1, 32, 4, 8, 4, 8, 16
+    xf, w_qkv, w_o = _layer_inputs(B, S, D, Hq, Hkv, dh, dm, 92)
+    r = 1
+    pos = np.asarray(o.zigzag_positions(S, D, r))
+    kf = _rand((B, S, Hkv, dh), 93)
+    vf = _rand((B, S, Hkv, dh), 94)
+    y, _, _ = o.tsp_layer.attention_layer(xf[:, pos], w_qkv, w_o, kf, vf, D, r, Hq, Hkv, dh)
+    hs, hks = Hq // D, Hkv // D
+    total = np.zeros_like(y)
+    for i in range(D):
+        wq = w_qkv[i * hs * dh:(i + 1) * hs * dh]
+        wk = w_qkv[Hq * dh + i * hks * dh:Hq * dh + (i + 1) * hks * dh]
+        wv = w_qkv[(Hq + Hkv) * dh + i * hks * dh:(Hq + Hkv) * dh + (i + 1) * hks * dh]
+        wo = w_o[:, i * hs * dh:(i + 1) * hs * dh]
+        yi, _, _ = o.tsp_layer.attention_layer(xf[:, pos], np.concatenate([wq, wk, wv]), wo,
+                                               kf[:, :, i * hks:(i + 1) * hks], vf[:, :, i * hks:(i + 1) * hks],
+                                               D, r, hs, hks, dh)
+        total += yi
+    assert np.allclose(total, y, rtol=0, atol=1e-10)
+
+
 ALL_PINS = [
     pin_zigzag_golden,
     pin_zigzag_permutation,
@@ -479,4 +538,6 @@ ALL_PINS = [
     pin_bwd_gqa_and_subset,
     pin_ulysses_pack_elementwise,
     pin_ulysses_round_trip_and_heads,
+    pin_layer_unsharded,
+    pin_layer_shard_sum,
 ]

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as A
+import oracle.tsp_layer as L
 import oracle.ulysses as U
 from pins import ALL_PINS
 
@@ -91,6 +92,7 @@ def _namespace():
               "causal_attention_backward"):
         setattr(ns, n, getattr(A, n))
     ns.ulysses = U
+    ns.tsp_layer = L
     return ns
 
 
@@ -252,3 +254,39 @@ def test_ulysses_mutant_is_caught(kind):
     ns.ulysses = _ulysses_mutant(kind)
     failed = [f for f in _failures(ns) if f.startswith("pin_ulysses")]
     assert failed, f"Ulysses mutant {kind} passed every Ulysses pin"
+
+
+def _layer_mutant(kind):
+    """A copy of the layer oracle with one plausible mistake."""
+    def layer(x_local, w_qkv, w_o, k_gathered, v_gathered, D, rank, Hq, Hkv, dh):
+        x, W, Wo = (np.asarray(t, dtype=np.float64) for t in (x_local, w_qkv, w_o))
+        B, S_local, dm = x.shape
+        K = np.array(k_gathered, dtype=np.float64)
+        V = np.array(v_gathered, dtype=np.float64)
+        q = (x @ W[:Hq * dh].T).reshape(B, S_local, Hq, dh)
+        k_loc = (x @ W[Hq * dh:(Hq + Hkv) * dh].T).reshape(B, S_local, Hkv, dh)
+        v_loc = (x @ W[(Hq + Hkv) * dh:].T).reshape(B, S_local, Hkv, dh)
+        pos = A.zigzag_positions(K.shape[1], D, rank)
+        if kind == "local_rows_not_placed":
+            pass
+        elif kind == "placed_at_local_rows":
+            K[:, :S_local] = k_loc
+            V[:, :S_local] = v_loc
+        else:
+            K[:, pos] = k_loc
+            V[:, pos] = v_loc
+        if kind == "k_v_weights_swapped":
+            K[:, pos], V[:, pos] = v_loc, k_loc
+        o, _ = A.causal_attention(q, K, V, D, rank)
+        y = o.reshape(B, S_local, Hq * dh) @ (Wo if kind == "w_o_untransposed" and Wo.shape[0] == Wo.shape[1] else Wo.T)
+        return y, K, V
+    return layer
+
+
+@pytest.mark.parametrize("kind", ["local_rows_not_placed", "placed_at_local_rows", "k_v_weights_swapped"])
+def test_layer_mutant_is_caught(kind):
+    ns = _namespace()
+    ns.tsp_layer = types.SimpleNamespace(attention_layer=_layer_mutant(kind))
+    with np.errstate(all="ignore"):
+        failed = [f for f in _failures(ns) if f.startswith("pin_layer")]
+    assert failed, f"layer mutant {kind} passed every layer pin"
