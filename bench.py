@@ -93,6 +93,59 @@ def cpu_baseline(w, rank, q, k, v, budget_s: float):
     }
 
 
+def layer_bench(args, torch, tsp, workloads):
+    """One rank's TSP attention layer forward on the workload's shard (weights synthetic)."""
+    w = workloads.BY_NAME[args.workload]
+    rank = w.ranks[0] if args.rank is None else args.rank
+    dm = args.layer
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = (workloads.make_grad((w.B, w.S_local, dm), 11, torch.float32) / dm ** 0.5).to(torch.bfloat16).to(dev)
+    w_qkv = workloads.make_grad(((w.Hq + 2 * w.Hkv) * w.dh, dm), 12, torch.bfloat16).to(dev)
+    w_o = (workloads.make_grad((dm, w.Hq * w.dh), 13, torch.float32) / (w.Hq * w.dh) ** 0.5).to(torch.bfloat16).to(dev)
+    _, k, v = workloads.make_inputs(w, rank)
+    kd, vd = k.to(dev), v.to(dev)
+    y = torch.empty_like(x)
+    ws = torch.empty(tsp.attn_layer_workspace_bytes(w.B, w.S_total, w.D, w.Hq, w.Hkv, w.dh, dm), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        tsp.attn_layer_fwd(x, w_qkv, w_o, kd, vd, D=w.D, rank=rank, Hq=w.Hq, Hkv=w.Hkv, dh=w.dh, y=y, workspace=ws,
+                           stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    rows = w.B * w.S_local
+    proj = 2.0 * rows * dm * (w.Hq + 2 * w.Hkv) * w.dh + 2.0 * rows * w.Hq * w.dh * dm
+    attn = 4.0 * w.B * w.Hq * w.dh * w.C * (w.S_total + 1)
+    flops = proj + attn
+    line = {
+        "metric": "TSP attention layer TFLOP/s per rank (1 GPU)", "value": round(flops / ms / 1e9, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "rank": rank, "d_model": dm, "Hq": w.Hq, "Hkv": w.Hkv, "dh": w.dh,
+                   "D": w.D, "projection_flops": proj, "attention_flops": attn,
+                   "form": f"{w.D} weight shards x (Q, K, V projections, attention, output projection)"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / kernel_ms / 1e9, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / kernel_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel_ms": round(kernel_ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def ulysses_bench(args, torch, tsp, workloads):
     """The local permutes of Ulysses sequence parallelism for one of P ranks (HBM-bound)."""
     name = args.workload if args.workload != "tsp_7b_shard_s32k" else "ulysses_head_subset_s128k"
@@ -170,6 +223,10 @@ def main():
                          "sequence gather of q, k, v before the attention, sequence scatter and head "
                          "unpack of its output after (the workload is the attention shape after the "
                          "exchange); reports GB/s moved")
+    ap.add_argument("--layer", type=int, default=0, metavar="D_MODEL",
+                    help="time one rank's TSP attention layer instead (projections with every weight "
+                         "shard, zigzag attention, output projection) at this model width; FLOPs of the "
+                         "projections plus the causal attention")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run plain device copies of MIB MiB (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -197,6 +254,8 @@ def main():
 
     if args.ulysses:
         return ulysses_bench(args, torch, tsp, workloads)
+    if args.layer:
+        return layer_bench(args, torch, tsp, workloads)
 
     w = workloads.BY_NAME[args.workload]
     rank = w.ranks[0] if args.rank is None else args.rank

@@ -177,6 +177,50 @@ int tsp_ulysses_scatter_sequence(const void* full, void* send, int64_t B, int64_
                                  int64_t Hl, int64_t dh, int64_t P, int dtype, void* stream);
 
 /*
+ * tsp_gemm_bf16_nt -- C = A B^T for bf16 A [M, K] (row stride lda) and B [N, K] (row stride
+ * ldb), fp32 accumulation; the projection products of the attention layer below.
+ *   mode 0: C is bf16 [M, N] (row stride ldc), the result rounded to nearest even;
+ *   mode 1: C is float32, the result stored; mode 2: C is float32, the result added to it.
+ * Device buffers, 16-byte aligned; K a multiple of 64; N, ldc multiples of 4; lda, ldb
+ * multiples of 8 and at most 2^24. Enqueued on `stream`; returns TSP_OK or TSP_EINVAL /
+ * TSP_ELAUNCH.
+ */
+int tsp_gemm_bf16_nt(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc, int mode, void* stream);
+
+/*
+ * tsp_attn_layer_fwd -- one rank's TSP attention layer forward ("Folding Tensor and
+ * Sequence Parallelism ...", section 2, attention layers): the ranks iterate over D weight
+ * shards (packed W_Q, W_K, W_V, W_O of H/D heads each, broadcast by their owner); for each
+ * shard every rank projects its own tokens, the K/V of all ranks are gathered along the
+ * sequence, the rank's queries attend causally (zigzag positions) to them, and the output
+ * projection of the shard's heads is accumulated. On one GPU the shards are resident and
+ * the gather's other rows are given: this call runs one rank's share of every step.
+ *   x_local     device bf16 [B, 2C, d_model], the rank's tokens in local row order
+ *   w_qkv       device bf16 [(Hq + 2*Hkv) * dh, d_model]: the rows of W_Q (query heads in
+ *               order), then W_K, then W_V (out_features x in_features); shard i holds
+ *               query heads i*Hq/D .. and KV heads i*Hkv/D ..
+ *   w_o         device bf16 [d_model, Hq * dh]
+ *   k_gathered, v_gathered  device bf16 [B, S_total, Hkv, dh]: the gathered K/V; rows at the
+ *               rank's global positions are overwritten with its own projections, the
+ *               others are read as given (the other ranks' rows)
+ *   y_local     device bf16 [B, 2C, d_model] (written): softmax(Q K^T / sqrt(dh)) V W_O^T
+ *               over all heads for the rank's tokens
+ *   workspace   device, at least tsp_attn_layer_workspace_bytes(...) bytes (caller-owned;
+ *               holds a shard's Q and attention output, its lse and the fp32 sum of the
+ *               output projection)
+ * Hq and Hkv divisible by D (whole heads per shard), d_model a multiple of 64, dh in
+ * {64, 128, 256}, other size rules as tsp_attn_fwd. Enqueued on `stream`; returns TSP_OK,
+ * TSP_EINVAL, TSP_EUNSUPPORTED or TSP_ELAUNCH.
+ */
+int tsp_attn_layer_workspace_bytes(int64_t B, int64_t S_total, int64_t D, int64_t Hq,
+                                   int64_t Hkv, int64_t dh, int64_t d_model, int64_t* bytes);
+int tsp_attn_layer_fwd(const void* x_local, const void* w_qkv, const void* w_o, void* k_gathered,
+                       void* v_gathered, void* y_local, void* workspace, int64_t workspace_bytes,
+                       int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq,
+                       int64_t Hkv, int64_t dh, int64_t d_model, void* stream);
+
+/*
  * tsp_attn_zigzag_positions -- the zigzag map on the host: writes g(i) for the 2C local
  * rows of `rank` into out_host (caller-owned host memory of 2C int64).
  * ("Folding Tensor and Sequence Parallelism ...", section 2, zigzag partitioning.)

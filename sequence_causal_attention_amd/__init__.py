@@ -41,6 +41,9 @@ SIGNATURES = {
                                           _I64, _I64, ctypes.c_int, ctypes.c_int, _VP]),
     "tsp_attn_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "tsp_attn_bwd": (ctypes.c_int, [_VP] * 10 + [_I64] * 7 + [ctypes.c_int, _VP]),
+    "tsp_gemm_bf16_nt": (ctypes.c_int, [_VP, _VP, _VP] + [_I64] * 6 + [ctypes.c_int, _VP]),
+    "tsp_attn_layer_workspace_bytes": (ctypes.c_int, [_I64] * 7 + [ctypes.POINTER(_I64)]),
+    "tsp_attn_layer_fwd": (ctypes.c_int, [_VP] * 7 + [_I64] * 9 + [_VP]),
     "tsp_ulysses_pack_heads": (ctypes.c_int, [_VP, _VP] + [_I64] * 5 + [ctypes.c_int, _VP]),
     "tsp_ulysses_unpack_heads": (ctypes.c_int, [_VP, _VP] + [_I64] * 5 + [ctypes.c_int, _VP]),
     "tsp_ulysses_gather_sequence": (ctypes.c_int, [_VP, _VP] + [_I64] * 5 + [ctypes.c_int, _VP]),
@@ -256,6 +259,62 @@ def ulysses_scatter_sequence(full: torch.Tensor, P: int, out=None, stream=None) 
         raise TspAttnError(TSP_EINVAL, "sequence length must be divisible by P")
     return _ulysses_call(lib().tsp_ulysses_scatter_sequence, full, (P, B, S // P, Hl, dh), B, S // P, Hl, dh, P,
                          out, stream)
+
+
+def gemm_nt(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None, accumulate=False, stream=None):
+    """C = A B^T (tsp_gemm_bf16_nt) for bf16 a [M, K], b [N, K]. ``out`` bf16 (stored) or
+    fp32 (stored, or added to when ``accumulate``)."""
+    for t in (a, b):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1:
+            raise TspAttnError(TSP_EINVAL, "a and b must be 2-D bf16 GPU tensors with unit column stride")
+    M, K = a.shape
+    N = b.shape[0]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if out is None else out
+    if out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1:
+        raise TspAttnError(TSP_EINVAL, "out must be [M, N] with unit column stride")
+    mode = 0 if out.dtype == torch.bfloat16 else (2 if accumulate else 1)
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(a.device):
+        _check(lib().tsp_gemm_bf16_nt(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, a.stride(0), b.stride(0),
+                                      out.stride(0), mode, handle))
+    return out
+
+
+def attn_layer_workspace_bytes(B, S_total, D, Hq, Hkv, dh, d_model) -> int:
+    n = _I64(0)
+    _check(lib().tsp_attn_layer_workspace_bytes(B, S_total, D, Hq, Hkv, dh, d_model, ctypes.byref(n)))
+    return n.value
+
+
+def attn_layer_fwd(x_local: torch.Tensor, w_qkv: torch.Tensor, w_o: torch.Tensor, k_gathered: torch.Tensor,
+                   v_gathered: torch.Tensor, *, D: int, rank: int, Hq: int, Hkv: int, dh: int, y=None,
+                   workspace=None, stream=None):
+    """One rank's TSP attention layer forward (tsp_attn_layer_fwd). k_gathered / v_gathered
+    are updated in place at the rank's positions. Returns y_local [B, 2C, d_model]."""
+    ts = (x_local, w_qkv, w_o, k_gathered, v_gathered)
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise TspAttnError(TSP_EINVAL, "layer tensors must be contiguous bf16 GPU tensors")
+    B, S_local, d_model = x_local.shape
+    S_total = k_gathered.shape[1]
+    if tuple(w_qkv.shape) != ((Hq + 2 * Hkv) * dh, d_model) or tuple(w_o.shape) != (d_model, Hq * dh):
+        raise TspAttnError(TSP_EINVAL, "weight shapes do not match Hq, Hkv, dh, d_model")
+    if tuple(k_gathered.shape) != (B, S_total, Hkv, dh) or v_gathered.shape != k_gathered.shape:
+        raise TspAttnError(TSP_EINVAL, "gathered K/V must be [B, S_total, Hkv, dh]")
+    y = torch.empty_like(x_local) if y is None else y
+    nbytes = attn_layer_workspace_bytes(B, S_total, D, Hq, Hkv, dh, d_model)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_local.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x_local.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(x_local.device):
+        _check(lib().tsp_attn_layer_fwd(x_local.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(), k_gathered.data_ptr(),
+                                        v_gathered.data_ptr(), y.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                        B, S_total, D, rank, Hq, Hkv, dh, d_model, handle))
+    return y
 
 
 def fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, S_total, D, rank, Hq, Hkv, dh, dtype, stream) -> int:

@@ -53,13 +53,6 @@ struct TspBwdParams {
   float scale;          // 1 / sqrt(dh)
 };
 
-// s_waitcnt with vmcnt = N (0..63), other counters untouched.
-template <int N>
-__device__ __forceinline__ void tsp_wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
 // 4 bytes per lane from global memory straight into LDS: lane i reads *gaddr and writes
 // lds_addr + 4*i (global_load_lds_dword, address form, LDS base in M0).
 #pragma clang diagnostic push

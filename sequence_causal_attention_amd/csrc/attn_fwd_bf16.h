@@ -86,6 +86,13 @@ __device__ __forceinline__ void tsp_wait_vmcnt(int n) {
   }
 }
 
+// s_waitcnt with vmcnt = N (0..63), other counters untouched.
+template <int N>
+__device__ __forceinline__ void tsp_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane i reads sbase + voff
 // (sbase wave-uniform, voff its own byte offset) and writes lds_addr + 16*i (gfx950
 // global_load_lds_dwordx4, saddr form, LDS base in M0). Issued as inline asm on purpose:
@@ -163,13 +170,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
   const int32_t hk = unit % p.Hkv;
   const int32_t b = unit / p.Hkv;
 
-  const int64_t kv_row_stride = (int64_t)p.Hkv * DH;  // elements between consecutive keys
+  const int64_t kv_row_stride = p.kv_stride;  // elements between consecutive keys
   // The sweep starts at the stage boundary at or below kv_lo; key indices below are
   // relative to it (keys in [kv_base, kv_lo) are loaded but masked).
   const int32_t kv_base = (p.kv_lo / St::BKS) * St::BKS;
   const int32_t kv_lo_rel = p.kv_lo - kv_base;
-  const uint16_t* __restrict__ kbase = kg + (((int64_t)b * p.S_total + kv_base) * p.Hkv + hk) * DH;
-  const uint16_t* __restrict__ vbase = vg + (((int64_t)b * p.S_total + kv_base) * p.Hkv + hk) * DH;
+  const uint16_t* __restrict__ kbase = kg + ((int64_t)b * p.S_total + kv_base) * p.kv_stride + (int64_t)hk * DH;
+  const uint16_t* __restrict__ vbase = vg + ((int64_t)b * p.S_total + kv_base) * p.kv_stride + (int64_t)hk * DH;
   const int pos_blocks = p.BQ / 32;  // row blocks per head in a tile
 
   // ---- per-lane LDS read offsets (constant over the sweep) ------------------------------

@@ -43,9 +43,9 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(TspParams p) {
   const int32_t hk = unit % p.Hkv;
   const int32_t b = unit / p.Hkv;
 
-  const int64_t kv_row_stride = (int64_t)p.Hkv * DH;
-  const float* __restrict__ kbase = kg + ((int64_t)b * p.S_total * p.Hkv + hk) * DH;
-  const float* __restrict__ vbase = vg + ((int64_t)b * p.S_total * p.Hkv + hk) * DH;
+  const int64_t kv_row_stride = p.kv_stride;
+  const float* __restrict__ kbase = kg + (int64_t)b * p.S_total * p.kv_stride + (int64_t)hk * DH;
+  const float* __restrict__ vbase = vg + (int64_t)b * p.S_total * p.kv_stride + (int64_t)hk * DH;
   const int pos_blocks = p.BQ / 32;
 
   for (int which = 0; which < 2; ++which) {

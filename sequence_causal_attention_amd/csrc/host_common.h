@@ -95,6 +95,7 @@ inline int plan_tiles(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64
   p->kv_lo = 0;
   p->kv_hi = (int32_t)S_total;
   p->accumulate = 0;
+  p->kv_stride = Hkv * dh;
   p->scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   return TSP_OK;
 }

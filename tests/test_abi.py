@@ -22,7 +22,7 @@ HEADER = os.path.join(ROOT, "include", "tsp_attn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tsp_(?:attn|ulysses)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tsp_(?:attn|ulysses|gemm)_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -234,6 +234,31 @@ def test_ulysses_heads_must_divide(lib):
     f = _fake()
     assert lib.tsp_ulysses_pack_heads(f, f, 1, 16, 6, 128, 4, tsp.TSP_BF16, None) == tsp.TSP_EINVAL
     assert lib.tsp_ulysses_unpack_heads(f, f, 1, 16, 6, 128, 4, tsp.TSP_BF16, None) == tsp.TSP_EINVAL
+
+
+@pytest.mark.parametrize("args", [
+    (64, 64, 100, 128, 128, 64, 0),   # K not a multiple of 64
+    (64, 62, 128, 128, 128, 64, 0),   # N not a multiple of 4
+    (64, 64, 128, 64, 128, 64, 0),    # lda < K
+    (0, 64, 128, 128, 128, 64, 0),    # M = 0
+    (64, 64, 128, 128, 128, 64, 3),   # mode
+])
+def test_gemm_invalid_arguments_rejected(lib, args):
+    f = _fake()
+    assert lib.tsp_gemm_bf16_nt(f, f, f, *args, None) == tsp.TSP_EINVAL
+    assert lib.tsp_attn_last_error().decode() != ""
+
+
+def test_attn_layer_validation(lib):
+    n = ctypes.c_int64(0)
+    assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 8, 4, 128, 512, ctypes.byref(n)) == tsp.TSP_OK
+    rows, hs = 1 * 2048 // 4, 8 // 4
+    assert n.value >= rows * hs * 128 * 2 * 2 + rows * hs * 4 + rows * 512 * 4
+    assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 6, 2, 128, 512, ctypes.byref(n)) == tsp.TSP_EINVAL
+    assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 8, 4, 128, 500, ctypes.byref(n)) == tsp.TSP_EINVAL
+    f = _fake()
+    assert lib.tsp_attn_layer_fwd(f, f, f, f, f, f, f, 16, 1, 2048, 4, 1, 8, 4, 128, 512, None) == tsp.TSP_EINVAL
+    assert "workspace" in lib.tsp_attn_last_error().decode()
 
 
 def test_map_helpers_reject_bad_sizes(lib):
