@@ -106,14 +106,15 @@ def layer_bench(args, torch, tsp, workloads):
     _, k, v = workloads.make_inputs(w, rank)
     kd, vd = k.to(dev), v.to(dev)
     y = torch.empty_like(x)
-    ws = torch.empty(tsp.attn_layer_workspace_bytes(w.B, w.S_total, w.D, w.Hq, w.Hkv, w.dh, dm), dtype=torch.uint8,
+    G = args.layer_group
+    ws = torch.empty(tsp.attn_layer_workspace_bytes(w.B, w.S_total, w.D, w.Hq, w.Hkv, w.dh, dm, G), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.Stream(dev)
     torch.cuda.synchronize()
 
     def step():
-        tsp.attn_layer_fwd(x, w_qkv, w_o, kd, vd, D=w.D, rank=rank, Hq=w.Hq, Hkv=w.Hkv, dh=w.dh, y=y, workspace=ws,
-                           stream=stream)
+        tsp.attn_layer_fwd(x, w_qkv, w_o, kd, vd, D=w.D, rank=rank, Hq=w.Hq, Hkv=w.Hkv, dh=w.dh, shards_per_group=G,
+                           y=y, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -136,7 +137,7 @@ def layer_bench(args, torch, tsp, workloads):
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "rank": rank, "d_model": dm, "Hq": w.Hq, "Hkv": w.Hkv, "dh": w.dh,
-                   "D": w.D, "projection_flops": proj, "attention_flops": attn,
+                   "D": w.D, "shards_per_group": G or "auto", "projection_flops": proj, "attention_flops": attn,
                    "form": f"{w.D} weight shards x (Q, K, V projections, attention, output projection)"},
         "roofline": {"bound": "mfma", "achieved": round(flops / kernel_ms / 1e9, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / kernel_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -227,6 +228,8 @@ def main():
                     help="time one rank's TSP attention layer instead (projections with every weight "
                          "shard, zigzag attention, output projection) at this model width; FLOPs of the "
                          "projections plus the causal attention")
+    ap.add_argument("--layer-group", type=int, default=0, metavar="G",
+                    help="with --layer: weight shards per projection / attention launch (0 = automatic)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run plain device copies of MIB MiB (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")

@@ -182,7 +182,7 @@ int tsp_ulysses_scatter_sequence(const void* full, void* send, int64_t B, int64_
  *   mode 0: C is bf16 [M, N] (row stride ldc), the result rounded to nearest even;
  *   mode 1: C is float32, the result stored; mode 2: C is float32, the result added to it.
  * Device buffers, 16-byte aligned; K a multiple of 64; N, ldc multiples of 4; lda, ldb
- * multiples of 8 and at most 2^24. Enqueued on `stream`; returns TSP_OK or TSP_EINVAL /
+ * multiples of 8 and at most 2^22. Enqueued on `stream`; returns TSP_OK or TSP_EINVAL /
  * TSP_ELAUNCH.
  */
 int tsp_gemm_bf16_nt(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
@@ -206,19 +206,29 @@ int tsp_gemm_bf16_nt(const void* a, const void* b, void* c, int64_t M, int64_t N
  *               others are read as given (the other ranks' rows)
  *   y_local     device bf16 [B, 2C, d_model] (written): softmax(Q K^T / sqrt(dh)) V W_O^T
  *               over all heads for the rank's tokens
- *   workspace   device, at least tsp_attn_layer_workspace_bytes(...) bytes (caller-owned;
- *               holds a shard's Q and attention output, its lse and the fp32 sum of the
- *               output projection)
+ *   workspace   device, at least tsp_attn_layer_workspace_bytes(...) bytes for the same
+ *               shards_per_group (caller-owned; holds a group's Q and attention output, its
+ *               lse and the fp32 sum of the output projection)
+ *   shards_per_group  G, a divisor of D: the shards are taken in order G at a time, one
+ *               projection GEMM (Q, K and V of the group's heads), one attention launch and
+ *               one output-projection GEMM per group. G = 1 is the shard-by-shard schedule;
+ *               a larger G lets one launch cover the CUs when a shard has few heads, at the
+ *               cost of a G times larger workspace. 0: the fewest shards whose attention
+ *               launch has a workgroup per CU of the current device (the workspace size for
+ *               0 covers any G).
+ * The result does not depend on G beyond fp32 summation order of the output projection.
  * Hq and Hkv divisible by D (whole heads per shard), d_model a multiple of 64, dh in
  * {64, 128, 256}, other size rules as tsp_attn_fwd. Enqueued on `stream`; returns TSP_OK,
  * TSP_EINVAL, TSP_EUNSUPPORTED or TSP_ELAUNCH.
  */
 int tsp_attn_layer_workspace_bytes(int64_t B, int64_t S_total, int64_t D, int64_t Hq,
-                                   int64_t Hkv, int64_t dh, int64_t d_model, int64_t* bytes);
+                                   int64_t Hkv, int64_t dh, int64_t d_model,
+                                   int64_t shards_per_group, int64_t* bytes);
 int tsp_attn_layer_fwd(const void* x_local, const void* w_qkv, const void* w_o, void* k_gathered,
                        void* v_gathered, void* y_local, void* workspace, int64_t workspace_bytes,
                        int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq,
-                       int64_t Hkv, int64_t dh, int64_t d_model, void* stream);
+                       int64_t Hkv, int64_t dh, int64_t d_model, int64_t shards_per_group,
+                       void* stream);
 
 /*
  * tsp_attn_zigzag_positions -- the zigzag map on the host: writes g(i) for the 2C local

@@ -42,8 +42,8 @@ SIGNATURES = {
     "tsp_attn_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "tsp_attn_bwd": (ctypes.c_int, [_VP] * 10 + [_I64] * 7 + [ctypes.c_int, _VP]),
     "tsp_gemm_bf16_nt": (ctypes.c_int, [_VP, _VP, _VP] + [_I64] * 6 + [ctypes.c_int, _VP]),
-    "tsp_attn_layer_workspace_bytes": (ctypes.c_int, [_I64] * 7 + [ctypes.POINTER(_I64)]),
-    "tsp_attn_layer_fwd": (ctypes.c_int, [_VP] * 7 + [_I64] * 9 + [_VP]),
+    "tsp_attn_layer_workspace_bytes": (ctypes.c_int, [_I64] * 8 + [ctypes.POINTER(_I64)]),
+    "tsp_attn_layer_fwd": (ctypes.c_int, [_VP] * 7 + [_I64] * 10 + [_VP]),
     "tsp_ulysses_pack_heads": (ctypes.c_int, [_VP, _VP] + [_I64] * 5 + [ctypes.c_int, _VP]),
     "tsp_ulysses_unpack_heads": (ctypes.c_int, [_VP, _VP] + [_I64] * 5 + [ctypes.c_int, _VP]),
     "tsp_ulysses_gather_sequence": (ctypes.c_int, [_VP, _VP] + [_I64] * 5 + [ctypes.c_int, _VP]),
@@ -282,17 +282,20 @@ def gemm_nt(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None, a
     return out
 
 
-def attn_layer_workspace_bytes(B, S_total, D, Hq, Hkv, dh, d_model) -> int:
+def attn_layer_workspace_bytes(B, S_total, D, Hq, Hkv, dh, d_model, shards_per_group=0) -> int:
     n = _I64(0)
-    _check(lib().tsp_attn_layer_workspace_bytes(B, S_total, D, Hq, Hkv, dh, d_model, ctypes.byref(n)))
+    _check(lib().tsp_attn_layer_workspace_bytes(B, S_total, D, Hq, Hkv, dh, d_model, shards_per_group,
+                                                ctypes.byref(n)))
     return n.value
 
 
 def attn_layer_fwd(x_local: torch.Tensor, w_qkv: torch.Tensor, w_o: torch.Tensor, k_gathered: torch.Tensor,
-                   v_gathered: torch.Tensor, *, D: int, rank: int, Hq: int, Hkv: int, dh: int, y=None,
-                   workspace=None, stream=None):
+                   v_gathered: torch.Tensor, *, D: int, rank: int, Hq: int, Hkv: int, dh: int, shards_per_group=0,
+                   y=None, workspace=None, stream=None):
     """One rank's TSP attention layer forward (tsp_attn_layer_fwd). k_gathered / v_gathered
-    are updated in place at the rank's positions. Returns y_local [B, 2C, d_model]."""
+    are updated in place at the rank's positions. ``shards_per_group``: weight shards per
+    projection / attention launch (a divisor of D; 0 = automatic). Returns y_local
+    [B, 2C, d_model]."""
     ts = (x_local, w_qkv, w_o, k_gathered, v_gathered)
     for t in ts:
         if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
@@ -304,8 +307,11 @@ def attn_layer_fwd(x_local: torch.Tensor, w_qkv: torch.Tensor, w_o: torch.Tensor
     if tuple(k_gathered.shape) != (B, S_total, Hkv, dh) or v_gathered.shape != k_gathered.shape:
         raise TspAttnError(TSP_EINVAL, "gathered K/V must be [B, S_total, Hkv, dh]")
     y = torch.empty_like(x_local) if y is None else y
-    nbytes = attn_layer_workspace_bytes(B, S_total, D, Hq, Hkv, dh, d_model)
+    if (not y.is_cuda or y.dtype != torch.bfloat16 or not y.is_contiguous()
+            or tuple(y.shape) != tuple(x_local.shape)):
+        raise TspAttnError(TSP_EINVAL, "y must be a contiguous bf16 GPU tensor shaped like x_local")
     if workspace is None:
+        nbytes = attn_layer_workspace_bytes(B, S_total, D, Hq, Hkv, dh, d_model, shards_per_group)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_local.device)
     if stream is None:
         stream = torch.cuda.current_stream(x_local.device)
@@ -313,7 +319,7 @@ def attn_layer_fwd(x_local: torch.Tensor, w_qkv: torch.Tensor, w_o: torch.Tensor
     with torch.cuda.device(x_local.device):
         _check(lib().tsp_attn_layer_fwd(x_local.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(), k_gathered.data_ptr(),
                                         v_gathered.data_ptr(), y.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                                        B, S_total, D, rank, Hq, Hkv, dh, d_model, handle))
+                                        B, S_total, D, rank, Hq, Hkv, dh, d_model, shards_per_group, handle))
     return y
 
 

@@ -28,6 +28,8 @@ UNITS = [
     # backward kernels, dh 256: the dK/dV accumulators fill the arch VGPRs, so MFMA
     # results stay in the accumulation registers
     (os.path.join(CSRC, "tsp_attn_bwd256.hip"), []),
+    # projection GEMM and the attention layer: MFMA accumulators in the accumulation registers
+    (os.path.join(CSRC, "tsp_layer.hip"), []),
 ]
 SOURCES = [u[0] for u in UNITS]
 HEADERS = [os.path.join(ROOT, "include", "tsp_attn.h")] + [

@@ -100,4 +100,10 @@ inline int plan_tiles(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64
   return TSP_OK;
 }
 
+// The attention forward of the library's main unit, for the other units: plan the launch
+// (validates sizes, dtype and head dim) and enqueue it.
+int attn_plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
+              TspParams* p);
+int attn_launch(const TspParams& p, int64_t dh, int dtype, hipStream_t stream);
+
 }  // namespace tsp_host

@@ -11,7 +11,6 @@
 #include "attn_fwd_f32.h"
 #include "attn_merge.h"
 #include "ulysses_permute.h"
-#include "gemm_bf16.h"
 #include "host_common.h"
 
 namespace tsp_host {
@@ -138,68 +137,44 @@ int ulysses_transpose(const char* what, const void* in, void* out, int64_t B, in
   return tsp_host::ok();
 }
 
-// Validates and launches one GEMM (C = A B^T, bf16 operands).
-int gemm_launch(const char* what, tsp::GemmParams gp, hipStream_t stream) {
-  if (!gp.a || !gp.b || !gp.c || (gp.mode == tsp::GEMM_ADD_F32_TO_BF16 && !gp.c2))
-    return fail(TSP_EINVAL, "%s: null pointer argument", what);
-  if (!aligned16(gp.a) || !aligned16(gp.b) || !aligned16(gp.c) || (gp.c2 && !aligned16(gp.c2)))
-    return fail(TSP_EINVAL, "%s: pointers must be 16-byte aligned", what);
-  if (gp.M < 1 || gp.N < 1 || gp.K < 1) return fail(TSP_EINVAL, "%s: M, N and K must be >= 1", what);
-  if (gp.K % tsp::GEMM_BK != 0) return fail(TSP_EINVAL, "%s: K must be a multiple of %d", what, tsp::GEMM_BK);
-  if (gp.N % 4 != 0 || gp.ldc % 4 != 0 || gp.c_col % 4 != 0)
-    return fail(TSP_EINVAL, "%s: N, ldc and the column offset must be multiples of 4", what);
-  if (gp.lda < gp.K || gp.ldb < gp.K || gp.ldc < gp.c_col + gp.N)
-    return fail(TSP_EINVAL, "%s: leading dimensions too small", what);
-  if (gp.lda % 8 != 0 || gp.ldb % 8 != 0) return fail(TSP_EINVAL, "%s: lda and ldb must be multiples of 8", what);
-  if (gp.lda > (int64_t(1) << 24) || gp.ldb > (int64_t(1) << 24)) return fail(TSP_EINVAL, "%s: lda / ldb above 2^24", what);
-  gp.n_tiles_n = (gp.N + tsp::GEMM_BN - 1) / tsp::GEMM_BN;
-  const int64_t tiles = (int64_t)((gp.M + tsp::GEMM_BM - 1) / tsp::GEMM_BM) * gp.n_tiles_n;
-  if (tiles > 0x7fffffff) return fail(TSP_EINVAL, "%s: problem too large", what);
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(tsp::gemm_nt_bf16_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, gp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(TSP_ELAUNCH, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
-  return TSP_OK;
-}
-
-// Workspace of the attention layer, in bytes, each piece 256-byte aligned.
-struct LayerWorkspace {
-  int64_t q, o, lse, y, total;
-};
-LayerWorkspace layer_workspace(int64_t B, int64_t S_total, int64_t D, int64_t Hq, int64_t dh, int64_t d_model) {
-  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  const int64_t rows = B * (S_total / D);  // B * 2C local tokens
-  const int64_t hs = Hq / D;
-  LayerWorkspace w{};
-  w.q = 0;
-  w.o = up(rows * hs * dh * 2);
-  w.lse = w.o + up(rows * hs * dh * 2);
-  w.y = w.lse + up(rows * hs * 4);
-  w.total = w.y + up(rows * d_model * 4);
-  return w;
-}
-
-int layer_check(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh,
-                int64_t d_model) {
-  int st = check_sizes(S_total, D, rank);
-  if (st != TSP_OK) return st;
-  if (B < 1 || Hq < 1 || Hkv < 1 || d_model < 1) return fail(TSP_EINVAL, "B, heads and d_model must be >= 1");
-  if (dh != 64 && dh != 128 && dh != 256) return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
-  if (Hq % Hkv != 0) return fail(TSP_EINVAL, "Hq not divisible by Hkv");
-  if (Hq % D != 0 || Hkv % D != 0)
-    return fail(TSP_EINVAL, "the weight shards split the heads: Hq and Hkv must be divisible by D");
-  if (d_model % 64 != 0) return fail(TSP_EINVAL, "d_model must be a multiple of 64");
-  if ((Hq + 2 * Hkv) * dh > (int64_t(1) << 22) || d_model > (int64_t(1) << 22) || Hq * dh > (int64_t(1) << 22))
-    return fail(TSP_EINVAL, "layer too wide");
-  return TSP_OK;
-}
-
 __global__ void zigzag_dump_kernel(int32_t* out, int32_t n, int32_t C, int32_t D, int32_t rank) {
   const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) out[i] = tsp_zigzag_position(i, C, D, rank);
 }
 
 }  // namespace
+
+namespace tsp_host {
+
+int attn_plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
+              TspParams* p) {
+  KernelShape ks{};
+  return plan(B, S_total, D, rank, Hq, Hkv, dh, dtype, p, &ks);
+}
+
+int attn_launch(const TspParams& p, int64_t dh, int dtype, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (dtype == TSP_BF16) {
+    switch (dh) {
+      case 64: launch_bf16<64>(p, stream); break;
+      case 128: launch_bf16<128>(p, stream); break;
+      case 256: launch_bf16<256>(p, stream); break;
+      default: return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
+    }
+  } else {
+    switch (dh) {
+      case 64: launch_f32<64>(p, stream); break;
+      case 128: launch_f32<128>(p, stream); break;
+      case 256: launch_f32<256>(p, stream); break;
+      default: return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TSP_ELAUNCH, "attention kernel launch failed: %s", hipGetErrorString(e));
+  return TSP_OK;
+}
+
+}  // namespace tsp_host
 
 extern "C" {
 
@@ -304,135 +279,6 @@ int tsp_ulysses_gather_sequence(const void* recv, void* full, int64_t B, int64_t
 int tsp_ulysses_scatter_sequence(const void* full, void* send, int64_t B, int64_t S_local, int64_t Hl, int64_t dh,
                                  int64_t P, int dtype, void* stream) {
   return ulysses_transpose("scatter_sequence", full, send, B, S_local, Hl, dh, P, dtype, false, false, stream);
-}
-
-int tsp_gemm_bf16_nt(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
-                     int64_t ldc, int mode, void* stream) {
-  if (mode != tsp::GEMM_STORE_BF16 && mode != tsp::GEMM_STORE_F32 && mode != tsp::GEMM_ADD_F32)
-    return fail(TSP_EINVAL, "gemm: mode must be 0 (bf16), 1 (fp32) or 2 (fp32, accumulate)");
-  if (M > 0x7fffffff || N > 0x7fffffff || K > 0x7fffffff) return fail(TSP_EINVAL, "gemm: sizes above 2^31");
-  tsp::GemmParams gp{};
-  gp.a = static_cast<const uint16_t*>(a);
-  gp.b = static_cast<const uint16_t*>(b);
-  gp.c = c;
-  gp.lda = lda;
-  gp.ldb = ldb;
-  gp.ldc = ldc;
-  gp.M = (int32_t)M;
-  gp.N = (int32_t)N;
-  gp.K = (int32_t)K;
-  gp.mode = mode;
-  int st = gemm_launch("gemm", gp, static_cast<hipStream_t>(stream));
-  return st == TSP_OK ? tsp_host::ok() : st;
-}
-
-int tsp_attn_layer_workspace_bytes(int64_t B, int64_t S_total, int64_t D, int64_t Hq, int64_t Hkv, int64_t dh,
-                                   int64_t d_model, int64_t* bytes) {
-  if (!bytes) return fail(TSP_EINVAL, "null output pointer");
-  int st = layer_check(B, S_total, D, 0, Hq, Hkv, dh, d_model);
-  if (st != TSP_OK) return st;
-  *bytes = layer_workspace(B, S_total, D, Hq, dh, d_model).total;
-  return tsp_host::ok();
-}
-
-int tsp_attn_layer_fwd(const void* x_local, const void* w_qkv, const void* w_o, void* k_gathered, void* v_gathered,
-                       void* y_local, void* workspace, int64_t workspace_bytes, int64_t B, int64_t S_total,
-                       int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int64_t d_model,
-                       void* stream) {
-  const void* ptrs[] = {x_local, w_qkv, w_o, k_gathered, v_gathered, y_local, workspace};
-  for (const void* ptr : ptrs) {
-    if (!ptr) return fail(TSP_EINVAL, "null pointer argument");
-    if (!aligned16(ptr)) return fail(TSP_EINVAL, "pointers must be 16-byte aligned");
-  }
-  int st = layer_check(B, S_total, D, rank, Hq, Hkv, dh, d_model);
-  if (st != TSP_OK) return st;
-  const LayerWorkspace ws = layer_workspace(B, S_total, D, Hq, dh, d_model);
-  if (workspace_bytes < ws.total)
-    return fail(TSP_EINVAL, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes, (long long)ws.total);
-  const int64_t hs = Hq / D, hks = Hkv / D;  // heads of one weight shard
-  const int64_t rows = B * (S_total / D);
-  uint8_t* wsp = static_cast<uint8_t*>(workspace);
-  void* q_ws = wsp + ws.q;
-  void* o_ws = wsp + ws.o;
-  float* lse_ws = reinterpret_cast<float*>(wsp + ws.lse);
-  void* y_acc = wsp + ws.y;
-  const uint16_t* x = static_cast<const uint16_t*>(x_local);
-  const uint16_t* wqkv = static_cast<const uint16_t*>(w_qkv);
-  const uint16_t* wo = static_cast<const uint16_t*>(w_o);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
-  // attention of one shard's heads: q_ws against the gathered K/V of its KV heads
-  TspParams ap{};
-  KernelShape ks{};
-  st = plan(B, S_total, D, rank, hs, hks, dh, TSP_BF16, &ap, &ks);
-  if (st != TSP_OK) return st;
-  ap.kv_stride = Hkv * dh;
-
-  for (int64_t i = 0; i < D; ++i) {  // the weight shards, in broadcast order
-    tsp::GemmParams g{};
-    g.a = x;
-    g.lda = d_model;
-    g.K = (int32_t)d_model;
-    g.M = (int32_t)rows;
-    g.ldb = d_model;
-    g.mode = tsp::GEMM_STORE_BF16;
-    // Q of the shard's query heads: [rows, hs*dh], the attention's q_local
-    g.b = wqkv + (i * hs * dh) * d_model;
-    g.N = (int32_t)(hs * dh);
-    g.c = q_ws;
-    g.ldc = hs * dh;
-    if ((st = gemm_launch("layer q projection", g, s)) != TSP_OK) return st;
-    // K and V of the shard's KV heads, written at the tokens' global positions
-    g.zigzag = 1;
-    g.S_total = (int32_t)S_total;
-    g.C = (int32_t)(S_total / (2 * D));
-    g.D = (int32_t)D;
-    g.rank = (int32_t)rank;
-    g.S_local = (int32_t)(S_total / D);
-    g.N = (int32_t)(hks * dh);
-    g.ldc = Hkv * dh;
-    g.c_col = i * hks * dh;
-    g.b = wqkv + (Hq * dh + i * hks * dh) * d_model;
-    g.c = k_gathered;
-    if ((st = gemm_launch("layer k projection", g, s)) != TSP_OK) return st;
-    g.b = wqkv + (Hq * dh + Hkv * dh + i * hks * dh) * d_model;
-    g.c = v_gathered;
-    if ((st = gemm_launch("layer v projection", g, s)) != TSP_OK) return st;
-    // causal attention of the shard's heads over the gathered K/V
-    ap.q = q_ws;
-    ap.k = static_cast<const uint16_t*>(k_gathered) + i * hks * dh;
-    ap.v = static_cast<const uint16_t*>(v_gathered) + i * hks * dh;
-    ap.out = o_ws;
-    ap.lse = lse_ws;
-    (void)hipGetLastError();
-    switch (dh) {
-      case 64: launch_bf16<64>(ap, s); break;
-      case 128: launch_bf16<128>(ap, s); break;
-      case 256: launch_bf16<256>(ap, s); break;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(TSP_ELAUNCH, "layer attention launch failed: %s", hipGetErrorString(e));
-    // output projection of the shard's heads, accumulated over the shards
-    tsp::GemmParams go{};
-    go.a = static_cast<const uint16_t*>(o_ws);
-    go.lda = hs * dh;
-    go.b = wo + i * hs * dh;
-    go.ldb = Hq * dh;
-    go.K = (int32_t)(hs * dh);
-    go.M = (int32_t)rows;
-    go.N = (int32_t)d_model;
-    go.ldc = d_model;
-    if (D == 1) {
-      go.c = y_local;
-      go.mode = tsp::GEMM_STORE_BF16;
-    } else {
-      go.c = y_acc;
-      go.c2 = y_local;
-      go.mode = i == 0 ? tsp::GEMM_STORE_F32 : (i == D - 1 ? tsp::GEMM_ADD_F32_TO_BF16 : tsp::GEMM_ADD_F32);
-    }
-    if ((st = gemm_launch("layer output projection", go, s)) != TSP_OK) return st;
-  }
-  return tsp_host::ok();
 }
 
 int tsp_attn_zigzag_positions(int64_t S_total, int64_t D, int64_t rank, int64_t* out_host) {

@@ -251,14 +251,20 @@ def test_gemm_invalid_arguments_rejected(lib, args):
 
 def test_attn_layer_validation(lib):
     n = ctypes.c_int64(0)
-    assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 8, 4, 128, 512, ctypes.byref(n)) == tsp.TSP_OK
     rows, hs = 1 * 2048 // 4, 8 // 4
-    assert n.value >= rows * hs * 128 * 2 * 2 + rows * hs * 4 + rows * 512 * 4
-    assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 6, 2, 128, 512, ctypes.byref(n)) == tsp.TSP_EINVAL
-    assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 8, 4, 128, 500, ctypes.byref(n)) == tsp.TSP_EINVAL
+    for G in (1, 2, 4, 0):
+        assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 8, 4, 128, 512, G, ctypes.byref(n)) == tsp.TSP_OK
+        g = 4 if G == 0 else G  # automatic: sized for any group
+        assert n.value >= rows * g * hs * 128 * 2 * 2 + rows * g * hs * 4 + rows * 512 * 4
+    assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 6, 2, 128, 512, 1, ctypes.byref(n)) == tsp.TSP_EINVAL
+    assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 8, 4, 128, 500, 1, ctypes.byref(n)) == tsp.TSP_EINVAL
+    assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 8, 4, 128, 512, 3, ctypes.byref(n)) == tsp.TSP_EINVAL
+    assert lib.tsp_attn_layer_workspace_bytes(1, 2048, 4, 8, 4, 128, 512, -1, ctypes.byref(n)) == tsp.TSP_EINVAL
     f = _fake()
-    assert lib.tsp_attn_layer_fwd(f, f, f, f, f, f, f, 16, 1, 2048, 4, 1, 8, 4, 128, 512, None) == tsp.TSP_EINVAL
+    assert lib.tsp_attn_layer_fwd(f, f, f, f, f, f, f, 16, 1, 2048, 4, 1, 8, 4, 128, 512, 1, None) == tsp.TSP_EINVAL
     assert "workspace" in lib.tsp_attn_last_error().decode()
+    assert lib.tsp_attn_layer_fwd(f, f, f, f, f, f, f, 1 << 30, 1, 2048, 4, 1, 8, 4, 128, 512, 3, None) == tsp.TSP_EINVAL
+    assert "shards_per_group" in lib.tsp_attn_last_error().decode()
 
 
 def test_map_helpers_reject_bad_sizes(lib):

@@ -39,6 +39,8 @@ GEMM_CASES = [  # (M, N, K, padded leading dims)
     (300, 200, 128, False),   # ragged tiles in M and N
     (1, 4, 64, False),
     (4096, 512, 4096, False),  # a shard's Q projection of the 7B shard
+    (4096, 4096, 256, False),  # enough 256 x 256 tiles for the big-tile kernel
+    (4000, 4100, 128, False),  # ... with ragged tails
     (257, 132, 192, True),    # strided operands and output
 ]
 
@@ -81,27 +83,34 @@ def _layer_inputs(B, S, D, Hq, Hkv, dh, dm, seed):
     return x, w_qkv, w_o, k, v
 
 
-LAYER_CASES = [  # (B, S_total, D, rank, Hq, Hkv, dh, d_model)
-    (1, 512, 4, 1, 8, 4, 64, 256),
-    (1, 1024, 2, 0, 4, 2, 128, 512),
-    (2, 256, 2, 1, 4, 4, 64, 128),
-    (1, 1200, 3, 2, 6, 3, 128, 384),   # ragged: C = 200
-    (1, 2048, 8, 3, 8, 8, 128, 256),   # D = 8, one query head per shard
-    (1, 1024, 1, 0, 4, 2, 128, 256),   # D = 1: one shard, the Ulysses layout
-    (1, 512, 2, 1, 4, 2, 256, 256),    # dh 256
+LAYER_CASES = [  # (B, S_total, D, rank, Hq, Hkv, dh, d_model, shards per group)
+    (1, 512, 4, 1, 8, 4, 64, 256, 1),
+    (1, 512, 4, 1, 8, 4, 64, 256, 2),
+    (1, 512, 4, 1, 8, 4, 64, 256, 4),
+    (1, 1024, 2, 0, 4, 2, 128, 512, 1),
+    (1, 1024, 2, 0, 4, 2, 128, 512, 0),
+    (2, 256, 2, 1, 4, 4, 64, 128, 1),
+    (1, 1200, 3, 2, 6, 3, 128, 384, 1),   # ragged: C = 200
+    (1, 1200, 3, 2, 6, 3, 128, 384, 3),
+    (1, 2048, 8, 3, 8, 8, 128, 256, 1),   # D = 8, one query head per shard
+    (1, 2048, 8, 3, 8, 8, 128, 256, 0),
+    (1, 1024, 1, 0, 4, 2, 128, 256, 0),   # D = 1: one shard, the Ulysses layout
+    (1, 512, 2, 1, 4, 2, 256, 256, 1),    # dh 256
+    (1, 512, 2, 1, 4, 2, 256, 256, 2),
 ]
 
 
-@pytest.mark.parametrize("case", LAYER_CASES, ids=lambda c: "B{}_S{}_D{}_r{}_H{}x{}_d{}_m{}".format(*c))
+@pytest.mark.parametrize("case", LAYER_CASES, ids=lambda c: "B{}_S{}_D{}_r{}_H{}x{}_d{}_m{}_G{}".format(*c))
 def test_layer_vs_oracle(case):
-    B, S, D, r, Hq, Hkv, dh, dm = case
+    B, S, D, r, Hq, Hkv, dh, dm, G = case
     _note(f"layer {case}")
     x, w_qkv, w_o, k, v = _layer_inputs(B, S, D, Hq, Hkv, dh, dm, seed=S + D + r)
     pos = oracle.zigzag_positions(S, D, r)
     k_in = k.clone()
     k_in[:, torch.as_tensor(pos)] = 77.0  # the rank's rows must be overwritten
     kd, vd = k_in.to(DEV), v.to(DEV)
-    y = tsp.attn_layer_fwd(x.to(DEV), w_qkv.to(DEV), w_o.to(DEV), kd, vd, D=D, rank=r, Hq=Hq, Hkv=Hkv, dh=dh)
+    y = tsp.attn_layer_fwd(x.to(DEV), w_qkv.to(DEV), w_o.to(DEV), kd, vd, D=D, rank=r, Hq=Hq, Hkv=Hkv, dh=dh,
+                           shards_per_group=G)
     torch.cuda.synchronize()
     ref_y, ref_k, ref_v = oracle.tsp_layer.attention_layer(x, w_qkv, w_o, k_in, v, D, r, Hq, Hkv, dh)
     got = _np(y)
@@ -116,14 +125,16 @@ def test_layer_vs_oracle(case):
     assert torch.equal(vd.cpu()[:, torch.as_tensor(other)], v[:, torch.as_tensor(other)])
 
 
-def test_layer_full_size_sampled_rows():
+@pytest.mark.parametrize("G", [0, 1])
+def test_layer_full_size_sampled_rows(G):
     """The 7B-dense shard's attention layer (d_model 4096, 32 heads of 128, 32K tokens,
     rank 3 of 8): every output column of sampled rows against the oracle's pieces."""
     B, S, D, r, Hq, Hkv, dh, dm = 1, 32768, 8, 3, 32, 32, 128, 4096
-    _note("layer full size")
+    _note(f"layer full size G={G}")
     x, w_qkv, w_o, k, v = _layer_inputs(B, S, D, Hq, Hkv, dh, dm, seed=5)
     kd, vd = k.to(DEV), v.to(DEV)
-    y = tsp.attn_layer_fwd(x.to(DEV), w_qkv.to(DEV), w_o.to(DEV), kd, vd, D=D, rank=r, Hq=Hq, Hkv=Hkv, dh=dh)
+    y = tsp.attn_layer_fwd(x.to(DEV), w_qkv.to(DEV), w_o.to(DEV), kd, vd, D=D, rank=r, Hq=Hq, Hkv=Hkv, dh=dh,
+                           shards_per_group=G)
     torch.cuda.synchronize()
     C = S // (2 * D)
     rows = np.concatenate([np.arange(0, 16), np.arange(C - 8, C + 8), np.arange(2 * C - 16, 2 * C)])
