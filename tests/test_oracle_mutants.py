@@ -283,7 +283,8 @@ def _layer_mutant(kind):
     return layer
 
 
-@pytest.mark.parametrize("kind", ["local_rows_not_placed", "placed_at_local_rows", "k_v_weights_swapped"])
+@pytest.mark.parametrize("kind", ["local_rows_not_placed", "placed_at_local_rows", "k_v_weights_swapped",
+                                  "w_o_untransposed"])
 def test_layer_mutant_is_caught(kind):
     ns = _namespace()
     ns.tsp_layer = types.SimpleNamespace(attention_layer=_layer_mutant(kind))
