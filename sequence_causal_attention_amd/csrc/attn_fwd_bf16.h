@@ -18,7 +18,7 @@
 //    column, so row max / row sum are in-lane plus one swap of the two 32-lane halves,
 //    and the fp32 accumulator, rounded to bf16, is already the B operand of
 //    O^T = V^T P^T. Q^T stays in registers for the whole key sweep.
-//  * K/V are staged in 32-key stages straight from global memory into LDS
+//  * K/V are staged in 32 * SPS-key stages straight from global memory into LDS
 //    (global_load_lds_dwordx4, no register round trip) through a ring of NBUF stages,
 //    PD = NBUF-2 stages ahead of use; every wave issues an equal share of each stage and
 //    waits (vmcnt) only for the stage it needs next. Rows are XOR-swizzled at 16-byte
@@ -124,6 +124,11 @@ struct Bf16Stage {
   static constexpr int WL = TILE_BYTES / 1024;       // wave-loads per K (or V) tile
   static constexpr int LPW = 2 * WL / NW;            // wave-loads per wave per stage
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  // Ring layout: the K tiles of all slots first, then the V tiles, so four of the five
+  // slots of each lie within the 16-bit DS offset of one per-lane base register (no
+  // address add per read).
+  static constexpr int SLOT_STRIDE = TILE_BYTES;
+  static constexpr int V_BASE = NBUF * TILE_BYTES;
   static constexpr int PD = NBUF - 2;                // prefetch distance in stages
   static constexpr int SWZ = CPR < 16 ? CPR : 16;    // swizzle period (chunks)
   static_assert((2 * WL) % NW == 0, "stage loads must split evenly over the waves");
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int chunk = db * 4 + 2 * (g & 1) + ((s & 3) >> 1);
-      voff[db] = vrow * St::ROW_BYTES + ((chunk ^ xv) << 4) + ((s & 1) << 3);
+      voff[db] = St::V_BASE + vrow * St::ROW_BYTES + ((chunk ^ xv) << 4) + ((s & 1) << 3);
     }
   }
 
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     dma_row[q] = row;
     dma_isv[q] = isv;
     dma_voff[q] = (uint32_t)(row * row_bytes_g + c * 16);
-    dma_slot[q] = (isv ? St::TILE_BYTES : 0) + j * 1024;
+    dma_slot[q] = (isv ? St::V_BASE : 0) + j * 1024;
   }
   const uint32_t smem_addr = __builtin_amdgcn_readfirstlane(tsp_lds_addr(smem));
   const float inv_scale_log2 = 1.0f / p.scale_log2;
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     // Any stage: rows past the tile's last position are clamped to it (never read past it).
     auto issue_stage = [&](int s) {
       const int32_t kv0 = s * St::BKS;
-      const uint32_t base = smem_addr + (s % NBUF) * St::STAGE_BYTES;
+      const uint32_t base = smem_addr + (s % NBUF) * St::SLOT_STRIDE;
 #pragma unroll
       for (int q = 0; q < St::LPW; ++q) {
         const int32_t over = max(0, kv0 + dma_row[q] - (kv_end - 1));  // rows beyond the last key
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     // ---- pipeline pieces ---------------------------------------------------------------
     // step t reads keys [32t, 32t+32): stage t/SPS, rows 32*(t%SPS) .. of its slot
     auto qk = [&](int t, tsp_f32x16(&sc)[RB]) {
-      const uint8_t* kt = smem + ((t / SPS) % NBUF) * St::STAGE_BYTES + (t % SPS) * BK * St::ROW_BYTES;
+      const uint8_t* kt = smem + ((t / SPS) % NBUF) * St::SLOT_STRIDE + (t % SPS) * BK * St::ROW_BYTES;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -431,7 +436,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     };
     auto pv = [&](int t, const tsp_bf16x8(&pf)[RB][2]) {
       const uint8_t* vt =
-          smem + ((t / SPS) % NBUF) * St::STAGE_BYTES + St::TILE_BYTES + (t % SPS) * BK * St::ROW_BYTES;
+          smem + ((t / SPS) % NBUF) * St::SLOT_STRIDE + (t % SPS) * BK * St::ROW_BYTES;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -476,7 +481,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // that stage landed (this wave's part)
       __syncthreads();  // ... for every wave; the slot two stages back is free again
       const int64_t adv = (int64_t)(t0 / SPS + NEXT + PD) * stage_stride;
-      const uint32_t base = smem_addr + ((NEXT + PD) % NBUF) * St::STAGE_BYTES;
+      const uint32_t base = smem_addr + ((NEXT + PD) % NBUF) * St::SLOT_STRIDE;
 #pragma unroll
       for (int q = 0; q < St::LPW; ++q)
         tsp_lds_dma16((dma_isv[q] ? vbase : kbase) + adv, dma_voff[q], base + dma_slot[q]);
