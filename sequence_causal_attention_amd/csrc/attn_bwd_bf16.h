@@ -153,9 +153,16 @@ struct BwdQTile {
 
 // PIPE: issue the next step's S / dP products ahead of the current step's VALU work (one
 // more score tile live; off where the registers do not allow it).
-template <int DH, int NW, int NBUF, bool PIPE>
-__global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkv_bf16_kernel(TspBwdParams bp) {
+// MODE: which gradients one launch computes. Both (S, dP, P, dS, dV and dK) need about 300
+// registers per lane at dh 128, one wave per SIMD; dV alone (S, P, dV) and dK alone (S,
+// dP, P, dS, dK) each fit in 256, so two launches run at two waves per SIMD for 25% more
+// MFMA work (S is computed twice).
+enum BwdKvMode : int { BWD_KV_BOTH = 0, BWD_KV_DV = 1, BWD_KV_DK = 2 };
+
+template <int DH, int NW, int NBUF, bool PIPE, int MODE, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdParams bp) {
   using T = BwdQTile<DH, NW>;
+  constexpr bool DO_DV = MODE != BWD_KV_DK, DO_DK = MODE != BWD_KV_DV;
   constexpr int NDB = DH / 32, NKK = DH / 16, PD = NBUF - 1, KB = 32 * NW;
   constexpr int VM_STAGE = T::LPW + 1;  // loads per wave per stage (tiles + metadata)
   static_assert(PD >= 2 && VM_STAGE * (PD - 1) < 64, "ring depth / vmcnt range");
@@ -187,8 +194,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkv_bf16_kernel(TspBwdPar
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          *reinterpret_cast<tsp_u32x2*>(dkg + o_off + db * 32 + 8 * a) = tsp_u32x2{0u, 0u};
-          *reinterpret_cast<tsp_u32x2*>(dvg + o_off + db * 32 + 8 * a) = tsp_u32x2{0u, 0u};
+          if constexpr (DO_DK) *reinterpret_cast<tsp_u32x2*>(dkg + o_off + db * 32 + 8 * a) = tsp_u32x2{0u, 0u};
+          if constexpr (DO_DV) *reinterpret_cast<tsp_u32x2*>(dvg + o_off + db * 32 + 8 * a) = tsp_u32x2{0u, 0u};
         }
     }
     return;
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkv_bf16_kernel(TspBwdPar
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       kf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(kp + 16 * kk));
-      vf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(vp + 16 * kk));
+      if constexpr (DO_DK) vf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(vp + 16 * kk));
     }
   }
 
@@ -295,10 +302,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkv_bf16_kernel(TspBwdPar
       const tsp_bf16x8 qa = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(qs + qoff[kk]));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
     }
+    if constexpr (DO_DK) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const tsp_bf16x8 da = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(ds + qoff[kk]));
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const tsp_bf16x8 da = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(ds + qoff[kk]));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
+      }
     }
   };
 
@@ -342,22 +351,30 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkv_bf16_kernel(TspBwdPar
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       pw[v] = tsp_exp2(x[v]);
-      dsw[v] = pw[v] * (dp[v] - del[v]);
+      if constexpr (DO_DK) dsw[v] = pw[v] * (dp[v] - del[v]);
     }
     tsp_bf16x8 pf[2], dsf[2];
-    pf[0] = tsp_pack8(pw);
-    pf[1] = tsp_pack8(pw + 8);
-    dsf[0] = tsp_pack8(dsw);
-    dsf[1] = tsp_pack8(dsw + 8);
+    if constexpr (DO_DV) {
+      pf[0] = tsp_pack8(pw);
+      pf[1] = tsp_pack8(pw + 8);
+    }
+    if constexpr (DO_DK) {
+      dsf[0] = tsp_pack8(dsw);
+      dsf[1] = tsp_pack8(dsw + 8);
+    }
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int ro = st * 16 * T::ROW_BYTES;
-        const tsp_bf16x8 doT = tsp_tr_read8(ds + tlo[db] + ro, ds + thi[db] + ro);
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doT, pf[st], dv[db], 0, 0, 0);
-        const tsp_bf16x8 qT = tsp_tr_read8(qs + tlo[db] + ro, qs + thi[db] + ro);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf[st], dk[db], 0, 0, 0);
+        if constexpr (DO_DV) {
+          const tsp_bf16x8 doT = tsp_tr_read8(ds + tlo[db] + ro, ds + thi[db] + ro);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doT, pf[st], dv[db], 0, 0, 0);
+        }
+        if constexpr (DO_DK) {
+          const tsp_bf16x8 qT = tsp_tr_read8(qs + tlo[db] + ro, qs + thi[db] + ro);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf[st], dk[db], 0, 0, 0);
+        }
       }
   };
 
@@ -409,8 +426,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dkv_bf16_kernel(TspBwdPar
         wk[1] = tsp_pack_bf16(dk[db][4 * a + 2] * bp.scale, dk[db][4 * a + 3] * bp.scale);
         wv[0] = tsp_pack_bf16(dv[db][4 * a], dv[db][4 * a + 1]);
         wv[1] = tsp_pack_bf16(dv[db][4 * a + 2], dv[db][4 * a + 3]);
-        *reinterpret_cast<tsp_u32x2*>(dkg + o_off + db * 32 + 8 * a) = wk;
-        *reinterpret_cast<tsp_u32x2*>(dvg + o_off + db * 32 + 8 * a) = wv;
+        if constexpr (DO_DK) *reinterpret_cast<tsp_u32x2*>(dkg + o_off + db * 32 + 8 * a) = wk;
+        if constexpr (DO_DV) *reinterpret_cast<tsp_u32x2*>(dvg + o_off + db * 32 + 8 * a) = wv;
       }
   }
 }

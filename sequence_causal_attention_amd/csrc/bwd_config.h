@@ -17,10 +17,15 @@
 #ifndef TSP_BWD_Q_NW
 #define TSP_BWD_Q_NW 4
 #endif
+#ifndef TSP_BWD_KV_SPLIT
+#define TSP_BWD_KV_SPLIT 1
+#endif
 template <int DH>
 struct BwdCfg {
   static constexpr int KV_NW = 4, KV_NBUF = DH <= 128 ? TSP_BWD_KV_NBUF : 4;
   static constexpr bool KV_PIPE = DH <= 128 && TSP_BWD_KV_PIPE;
+  // dK and dV in separate launches at two waves per SIMD (dh <= 128), or one launch
+  static constexpr bool KV_SPLIT = DH <= 128 && TSP_BWD_KV_SPLIT;
   static constexpr int Q_NW = DH <= 128 ? TSP_BWD_Q_NW : 4, Q_NBUF = 4, Q_OCC = DH <= 128 ? 2 : 1;
 };
 
@@ -34,7 +39,14 @@ void tsp_bwd_launch(const tsp::TspBwdParams& bp, int64_t kv_units, hipStream_t s
                      s, bp);
   hipLaunchKernelGGL((tsp::attn_bwd_dq_bf16_kernel<DH, C::Q_NW, C::Q_NBUF, C::Q_OCC>), dim3(bp.f.n_units),
                      dim3(C::Q_NW * 64), 0, s, bp);
-  hipLaunchKernelGGL((tsp::attn_bwd_dkv_bf16_kernel<DH, C::KV_NW, C::KV_NBUF, C::KV_PIPE>), dim3((unsigned)kv_units),
-                     dim3(C::KV_NW * 64), 0, s, bp);
+  if constexpr (C::KV_SPLIT) {
+    hipLaunchKernelGGL((tsp::attn_bwd_dkv_bf16_kernel<DH, C::KV_NW, C::KV_NBUF, C::KV_PIPE, tsp::BWD_KV_DV, 2>),
+                       dim3((unsigned)kv_units), dim3(C::KV_NW * 64), 0, s, bp);
+    hipLaunchKernelGGL((tsp::attn_bwd_dkv_bf16_kernel<DH, C::KV_NW, C::KV_NBUF, C::KV_PIPE, tsp::BWD_KV_DK, 2>),
+                       dim3((unsigned)kv_units), dim3(C::KV_NW * 64), 0, s, bp);
+  } else {
+    hipLaunchKernelGGL((tsp::attn_bwd_dkv_bf16_kernel<DH, C::KV_NW, C::KV_NBUF, C::KV_PIPE, tsp::BWD_KV_BOTH, 1>),
+                       dim3((unsigned)kv_units), dim3(C::KV_NW * 64), 0, s, bp);
+  }
 }
 
