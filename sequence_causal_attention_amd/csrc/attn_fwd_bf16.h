@@ -40,15 +40,6 @@
 
 #include "attn_common.h"
 
-#ifndef TSP_SETPRIO
-#define TSP_SETPRIO 0
-#endif
-#ifndef TSP_SCHED
-#define TSP_SCHED 0
-#endif
-#ifndef TSP_QK_SPLIT
-#define TSP_QK_SPLIT 0
-#endif
 #ifndef TSP_PINGPONG
 #define TSP_PINGPONG 1
 #endif
@@ -335,29 +326,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
         kf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(kt + koff[kk]));
-#if TSP_QK_SPLIT
-      // two independent accumulation chains (even / odd reduction steps), summed at the end
-      tsp_f32x16 s2[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s2[rb][e] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NKK; kk += 2)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[rb][kk], sc[rb], 0, 0, 0);
-          s2[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk + 1], qf[rb][kk + 1], s2[rb], 0, 0, 0);
-        }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sc[rb] += s2[rb];
-#else
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[rb][kk], sc[rb], 0, 0, 0);
-#endif
     };
     // key kv_base + s*BK + 8(e/4) + 4*half + (e%4) of query column `col` is visible iff
     // it is <= qpos (the query's position, capped below kv_hi) and >= kv_lo
@@ -500,49 +473,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       if constexpr (!LAG && (U + 1) % SPS == 0)  // step t+1 opens a new stage
         boundary(std::integral_constant<int, (U + 1) / SPS>{}, t0);
       tsp_bf16x8 pf[RB][2];
-#if TSP_SETPRIO
-      __builtin_amdgcn_s_setprio(1);
-#endif
       qk(U + 1, sn);     // matrix pipe: next step's scores
-#if TSP_SETPRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
       softmax(sc, pf, false);  // vector pipe: this step's weights
-#if TSP_SETPRIO
-      __builtin_amdgcn_s_setprio(1);
-#endif
       pv(U, pf);         // matrix pipe: this step's output
-#if TSP_SETPRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
       if constexpr (LAG && (U + 2) % SPS == 0)  // the next stage's barrier, one phase early
         boundary(std::integral_constant<int, (U + 2) / SPS>{}, t0);
       rowmax(sn, mx);    // vector pipe: next step's row max
-#if TSP_SCHED == 1
-      // issue order: all operand reads, then QK MFMAs each followed by a slice of the
-      // softmax, then PV MFMAs each followed by a slice of the row max
-      __builtin_amdgcn_sched_group_barrier(0x100, NKK, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2 * NDB, 0);
-      for (int i = 0; i < NKK * RB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-      }
-      for (int i = 0; i < 2 * NDB * RB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      }
-#elif TSP_SCHED == 2
-      for (int i = 0; i < NKK * RB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-      }
-      for (int i = 0; i < 2 * NDB * RB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      }
-#endif
     };
     auto fast_group = [&]<int... Us>(std::integer_sequence<int, Us...>, auto lag_const, int t0) {
       (fast_step(std::integral_constant<int, Us>{}, lag_const, t0), ...);
