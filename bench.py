@@ -236,8 +236,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the per-rank attention on a single "
-              "MI355X and has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the per-rank attention runs on a single MI355X and "
+              "there is no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
