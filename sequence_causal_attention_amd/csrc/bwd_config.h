@@ -15,7 +15,7 @@
 #define TSP_BWD_KV_PIPE 0
 #endif
 #ifndef TSP_BWD_Q_NW
-#define TSP_BWD_Q_NW 4
+#define TSP_BWD_Q_NW 8
 #endif
 #ifndef TSP_BWD_KV_SPLIT
 #define TSP_BWD_KV_SPLIT 1
