@@ -82,15 +82,80 @@ def cpu_baseline(w, rank, q, k, v, budget_s: float):
             break
     dt = (time.perf_counter() - t0) / done
     flops = 4.0 * w.B * len(heads) * w.dh * pairs
+    host = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            host = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(min(threads, len(os.sched_getaffinity(0)))),
+        "host": host,
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle, rank {rank} rows [0,{n_rows}) and [{w.C},{w.C + n_rows}) "
                    f"(both chunks), query heads {heads}, all visible keys; {done} pass(es), "
                    f"{dt:.2f} s each; same algorithmic FLOP count convention"),
     }
+
+
+def step_stats(torch, stream, step, n=20):
+    """Per-step times (HIP events on the launch stream) of n further steps, after the
+    timed region: median and min in microseconds."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    return {"median": round(us[n // 2], 1), "min": round(us[0], 1), "n": n}
+
+
+def balance_bench(args, torch, tsp, workloads):
+    """Forward time of several ranks of one workload, each timed like the main benchmark:
+    the zigzag split should give every rank the same time."""
+    w = workloads.BY_NAME[args.workload]
+    ranks = list(range(w.D)) if args.balance == "all" else [int(x) for x in args.balance.split(",")]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)
+    flops = 4.0 * w.B * w.Hq * w.dh * w.C * (w.S_total + 1)
+    per = {}
+    for r in ranks:
+        q, k, v = workloads.make_inputs(w, r)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        out = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.Hq, w.S_local), dtype=torch.float32, device=dev)
+
+        def step():
+            tsp.fwd(qd, kd, vd, D=w.D, rank=r, out=out, lse=lse, stream=stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
+        per[str(r)] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                       "launch_us": step_stats(torch, stream, step, n=min(20, max(5, args.steps)))}
+        del qd, kd, vd, out, lse
+        torch.cuda.empty_cache()
+    times = [e["ms"] for e in per.values()]
+    line = {
+        "metric": "per-rank forward time, max / min over the ranks timed (1 GPU)",
+        "value": round(max(times) / min(times), 4), "unit": "ratio", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S_total": w.S_total, "D": w.D, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "dh": w.dh, "flops_per_rank": flops, "ranks": per},
+    }
+    print(json.dumps(line), flush=True)
 
 
 def layer_bench(args, torch, tsp, workloads):
@@ -230,6 +295,9 @@ def main():
                          "projections plus the causal attention")
     ap.add_argument("--layer-group", type=int, default=0, metavar="G",
                     help="with --layer: weight shards per projection / attention launch (0 = automatic)")
+    ap.add_argument("--balance", default=None, metavar="RANKS",
+                    help="time the forward of several ranks of the workload instead (comma list, or "
+                         "'all'); reports each rank's time and the max / min ratio")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run plain device copies of MIB MiB (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -255,6 +323,8 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": max(1, args.steps)}), flush=True)
         return
 
+    if args.balance:
+        return balance_bench(args, torch, tsp, workloads)
     if args.ulysses:
         return ulysses_bench(args, torch, tsp, workloads)
     if args.layer:
@@ -315,6 +385,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    launch = step_stats(torch, stream, step)
 
     # causal FLOPs: 2 products (forward) or 5 (backward) of 2*dh per visible pair per query head
     flops = (10.0 if args.backward else 4.0) * w.B * w.Hq * w.dh * w.C * (w.S_total + 1)
@@ -360,6 +431,7 @@ def main():
             "traffic": None if (args.chunk_pipeline or args.backward) else measured_traffic(w.name, flops),
             "kernel_ms": round(kernel_ms, 4),
         },
+        "step_us": launch,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

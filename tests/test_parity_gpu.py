@@ -233,6 +233,30 @@ def test_gqa_equals_repeated_heads():
     assert np.abs(lse_g - lse_m).max() <= 2e-2
 
 
+@pytest.mark.parametrize("dh", [128, 256])
+def test_key_shift_invariance(dh):
+    """Adding one vector c to every key leaves out unchanged and shifts lse by
+    q_i . c / sqrt(dh). Keys and c lie on a 1/16 grid with |k + c| < 16, so k + c is exact
+    in bf16 and the property holds for the stored values; both runs are also checked
+    against the oracle."""
+    S, D, r, Hq, Hkv = 2048, 4, 1, 4, 2
+    q, k, v = workloads.make_custom(1, S, D, Hq, Hkv, dh, torch.bfloat16, seed=21 + dh)
+    k = (k.float() * 16).round().clamp(-96, 96).div(16).to(torch.bfloat16)
+    g = torch.Generator().manual_seed(5)
+    c = (torch.randn(Hkv, dh, generator=g) * 16).round().clamp(-32, 32).div(16)
+    k2 = (k.float() + c).to(torch.bfloat16)
+    assert torch.equal(k2.float() - k.float(), c.expand_as(k2.float()))  # exact in bf16
+    out1, lse1 = run(q, k, v, D, r)
+    out2, lse2 = run(q, k2, v, D, r)
+    grp = Hq // Hkv
+    shift = np.einsum("bshd,hd->bhs", q.double().numpy(), c.double().numpy().repeat(grp, axis=0)) / math.sqrt(dh)
+    assert np.abs(out2 - out1).max() <= 2e-2
+    assert np.abs(lse2 - lse1 - shift).max() <= 2e-2
+    for kk, out, lse in ((k, out1, lse1), (k2, out2, lse2)):
+        ref_out, ref_lse = oracle.causal_attention(q, kk, v, D, r)
+        check(out, lse, ref_out, ref_lse, torch.bfloat16, C=S // (2 * D))
+
+
 def test_deterministic_bitwise():
     q, k, v = workloads.make_custom(1, 8192, 8, 8, 2, 128, torch.bfloat16, seed=13)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
