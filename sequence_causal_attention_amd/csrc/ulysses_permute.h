@@ -32,13 +32,7 @@ struct BlockTransposeParams {
   uint32_t total;     // M * N * cpb chunks
 };
 
-#ifndef TSP_PERMUTE_UNROLL
-#define TSP_PERMUTE_UNROLL 2
-#endif
-#ifndef TSP_PERMUTE_NT
-#define TSP_PERMUTE_NT 0
-#endif
-constexpr int TSP_PERMUTE_U = TSP_PERMUTE_UNROLL;
+constexpr int TSP_PERMUTE_U = 2;  // output chunks per thread
 
 __global__ __launch_bounds__(256) void block_transpose_kernel(BlockTransposeParams p) {
   constexpr int U = TSP_PERMUTE_U;
@@ -57,11 +51,7 @@ __global__ __launch_bounds__(256) void block_transpose_kernel(BlockTransposePara
   for (int u = 0; u < U; ++u) {
     const uint32_t idx = base + 256u * u;
     if (idx < p.total) {
-#if TSP_PERMUTE_NT
-      __builtin_nontemporal_store(v[u], p.out + idx);  // streamed: not re-read by this kernel
-#else
       p.out[idx] = v[u];
-#endif
     }
   }
 }

@@ -10,12 +10,8 @@
 
 #include <stdint.h>
 
-#if defined(__HIPCC__)
-#define TSP_HD __host__ __device__ __forceinline__
-#else
-#define TSP_HD inline
-#endif
+#include <hip/hip_runtime.h>
 
-TSP_HD int32_t tsp_zigzag_position(int32_t row, int32_t C, int32_t D, int32_t rank) {
+__host__ __device__ __forceinline__ int32_t tsp_zigzag_position(int32_t row, int32_t C, int32_t D, int32_t rank) {
   return row < C ? rank * C + row : (2 * D - 1 - rank) * C + (row - C);
 }
