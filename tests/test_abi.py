@@ -110,6 +110,11 @@ def _call(lib, ptrs=None, **kw):
     (dict(dh=96), tsp.TSP_EUNSUPPORTED),
     (dict(dh=32), tsp.TSP_EUNSUPPORTED),
     (dict(dtype=7), tsp.TSP_EUNSUPPORTED),
+    # past the size limits: positions must stay int32, per-lane byte offsets 32-bit
+    (dict(S_total=1 << 31), tsp.TSP_EINVAL),
+    (dict(S_total=(1 << 30) + 8), tsp.TSP_EINVAL),
+    (dict(Hq=1 << 17, Hkv=1 << 17, dh=64), tsp.TSP_EINVAL),
+    (dict(B=1 << 17), tsp.TSP_EINVAL),
 ])
 def test_invalid_arguments_rejected(lib, kw, code):
     assert _call(lib, **kw) == code
