@@ -30,15 +30,17 @@ METRIC = "causal attention TFLOP/s per rank shard + % of bf16 MFMA peak (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-# the sources of the forward kernel and of its launch configuration
-FORWARD_SOURCES = ("attn_common.h", "attn_fwd_bf16.h", "attn_fwd_f32.h", "zigzag.h", "tsp_attn.hip")
+# the sources of the forward kernel and of its launch configuration, and the build script
+# that holds its compile flags
+FORWARD_SOURCES = ("csrc/attn_common.h", "csrc/attn_fwd_bf16.h", "csrc/attn_fwd_f32.h", "csrc/zigzag.h",
+                   "csrc/tsp_attn.hip", "build.py")
 
 
 def kernel_source_digest() -> str:
-    csrc = os.path.join(ROOT, "sequence_causal_attention_amd", "csrc")
+    pkg = os.path.join(ROOT, "sequence_causal_attention_amd")
     h = hashlib.sha256()
     for name in FORWARD_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(pkg, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
