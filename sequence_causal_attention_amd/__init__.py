@@ -89,6 +89,14 @@ def _check(status: int):
         raise TspAttnError(status, msg)
 
 
+def _on_device(device, **tensors):
+    """Every tensor must live on `device` (a host or other-device pointer would reach the
+    kernels as a wild address)."""
+    for name, t in tensors.items():
+        if not t.is_cuda or t.device != device:
+            raise TspAttnError(TSP_EINVAL, f"{name} must be on {device}")
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return TSP_BF16
@@ -139,6 +147,7 @@ def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D:
         raise TspAttnError(TSP_EINVAL, "out must match q_local")
     if tuple(lse.shape) != (B, Hq, S_local) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise TspAttnError(TSP_EINVAL, "lse must be float32 [B, Hq, S_local]")
+    _on_device(q_local.device, out=out, lse=lse)
     if stream is None:
         stream = torch.cuda.current_stream(q_local.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -161,13 +170,16 @@ def merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor, lse_b: 
     if out_a.shape != out_b.shape or out_a.dtype != out_b.dtype or out_a.dim() != 4:
         raise TspAttnError(TSP_EINVAL, "out_a / out_b must match, [B, S_local, Hq, dh]")
     B, S_local, Hq, dh = out_a.shape
-    if tuple(lse_a.shape) != (B, Hq, S_local) or lse_b.shape != lse_a.shape or lse_a.dtype != torch.float32:
+    if (tuple(lse_a.shape) != (B, Hq, S_local) or lse_b.shape != lse_a.shape or lse_a.dtype != torch.float32
+            or lse_b.dtype != torch.float32):
         raise TspAttnError(TSP_EINVAL, "lse_a / lse_b must be float32 [B, Hq, S_local]")
     code = _dtype_code(out_a)
     out = torch.empty_like(out_a) if out is None else out
     lse = torch.empty_like(lse_a) if lse is None else lse
-    if out.shape != out_a.shape or out.dtype != out_a.dtype or lse.shape != lse_a.shape:
+    if (out.shape != out_a.shape or out.dtype != out_a.dtype or lse.shape != lse_a.shape
+            or lse.dtype != torch.float32 or not out.is_contiguous() or not lse.is_contiguous()):
         raise TspAttnError(TSP_EINVAL, "out / lse must match the operands")
+    _on_device(out_a.device, lse_a=lse_a, out_b=out_b, lse_b=lse_b, out=out, lse=lse)
     if stream is None:
         stream = torch.cuda.current_stream(out_a.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -205,6 +217,8 @@ def bwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, out: 
     for name, t, ref in (("dq", dq, q_local), ("dk", dk, k_full), ("dv", dv, v_full), ("delta", delta, lse)):
         if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or not t.is_cuda:
             raise TspAttnError(TSP_EINVAL, f"{name} must match {tuple(ref.shape)} {ref.dtype}")
+    _on_device(q_local.device, k_full=k_full, v_full=v_full, out=out, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv,
+               delta=delta)
     if stream is None:
         stream = torch.cuda.current_stream(q_local.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -223,6 +237,7 @@ def _ulysses_call(fn, src: torch.Tensor, out_shape, B, S_local, H, dh, P, out=No
     out = torch.empty(out_shape, dtype=src.dtype, device=src.device) if out is None else out
     if tuple(out.shape) != tuple(out_shape) or out.dtype != src.dtype or not out.is_contiguous():
         raise TspAttnError(TSP_EINVAL, f"output must be contiguous {tuple(out_shape)} {src.dtype}")
+    _on_device(src.device, out=out)
     if stream is None:
         stream = torch.cuda.current_stream(src.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -272,6 +287,11 @@ def gemm_nt(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None, a
     out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if out is None else out
     if out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1:
         raise TspAttnError(TSP_EINVAL, "out must be [M, N] with unit column stride")
+    if out.dtype not in (torch.bfloat16, torch.float32) or (accumulate and out.dtype != torch.float32):
+        raise TspAttnError(TSP_EINVAL, "out must be bf16, or float32 (which accumulate needs)")
+    if b.shape[1] != K:
+        raise TspAttnError(TSP_EINVAL, "a and b must share K")
+    _on_device(a.device, b=b, out=out)
     mode = 0 if out.dtype == torch.bfloat16 else (2 if accumulate else 1)
     if stream is None:
         stream = torch.cuda.current_stream(a.device)
@@ -313,12 +333,17 @@ def attn_layer_fwd(x_local: torch.Tensor, w_qkv: torch.Tensor, w_o: torch.Tensor
     if workspace is None:
         nbytes = attn_layer_workspace_bytes(B, S_total, D, Hq, Hkv, dh, d_model, shards_per_group)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_local.device)
+    if not workspace.is_contiguous():
+        raise TspAttnError(TSP_EINVAL, "workspace must be contiguous")
+    _on_device(x_local.device, w_qkv=w_qkv, w_o=w_o, k_gathered=k_gathered, v_gathered=v_gathered, y=y,
+               workspace=workspace)
     if stream is None:
         stream = torch.cuda.current_stream(x_local.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(x_local.device):
         _check(lib().tsp_attn_layer_fwd(x_local.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(), k_gathered.data_ptr(),
-                                        v_gathered.data_ptr(), y.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                        v_gathered.data_ptr(), y.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
                                         B, S_total, D, rank, Hq, Hkv, dh, d_model, shards_per_group, handle))
     return y
 

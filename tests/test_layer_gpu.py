@@ -150,3 +150,20 @@ def test_layer_full_size_sampled_rows(G):
     ref = o.reshape(B, len(rows), Hq * dh) @ w_o.double().numpy().T
     got = _np(y[:, torch.as_tensor(rows)])
     assert _rel(got, ref) <= 2e-2 and np.abs(got - ref).max() <= 2.0 ** -4 * np.abs(ref).max()
+
+
+def test_layer_workspace_counted_in_bytes_and_on_device():
+    """A workspace of any element type is sized in bytes; one on the host is refused."""
+    B, S, D, r, Hq, Hkv, dh, dm = 1, 512, 2, 1, 4, 2, 64, 128
+    x, w_qkv, w_o, k, v = _layer_inputs(B, S, D, Hq, Hkv, dh, dm, seed=3)
+    nbytes = tsp.attn_layer_workspace_bytes(B, S, D, Hq, Hkv, dh, dm, 1)
+    args = (x.to(DEV), w_qkv.to(DEV), w_o.to(DEV))
+    kd1, vd1, kd2, vd2 = k.to(DEV), v.to(DEV), k.to(DEV), v.to(DEV)
+    y1 = tsp.attn_layer_fwd(*args, kd1, vd1, D=D, rank=r, Hq=Hq, Hkv=Hkv, dh=dh, shards_per_group=1)
+    ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=DEV)
+    y2 = tsp.attn_layer_fwd(*args, kd2, vd2, D=D, rank=r, Hq=Hq, Hkv=Hkv, dh=dh, shards_per_group=1, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    with pytest.raises(tsp.TspAttnError):
+        tsp.attn_layer_fwd(*args, kd1, vd1, D=D, rank=r, Hq=Hq, Hkv=Hkv, dh=dh, shards_per_group=1,
+                           workspace=torch.empty(nbytes, dtype=torch.uint8))

@@ -299,3 +299,30 @@ def test_invalid_call_writes_nothing():
     assert torch.all(out == 3.0) and torch.all(lse == 5.0)
     with pytest.raises(tsp.TspAttnError):
         tsp.fwd(qd, kd, vd, D=4, rank=4)
+
+
+def test_binding_rejects_host_and_mistyped_buffers():
+    """Caller-supplied outputs on the host, or of the wrong type, are refused before any
+    launch (their pointers would otherwise reach the kernels)."""
+    q, k, v = workloads.make_custom(1, 512, 4, 4, 1, 64, torch.bfloat16, seed=3)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse = tsp.fwd(qd, kd, vd, D=4, rank=1)
+    with pytest.raises(tsp.TspAttnError):
+        tsp.fwd(qd, kd, vd, D=4, rank=1, out=torch.empty_like(q), lse=lse)
+    with pytest.raises(tsp.TspAttnError):
+        tsp.fwd(qd, kd, vd, D=4, rank=1, out=out, lse=lse.cpu())
+    with pytest.raises(tsp.TspAttnError):
+        tsp.merge(out, lse, out, lse, out=out.cpu(), lse=lse)
+    dout = torch.zeros_like(qd)
+    with pytest.raises(tsp.TspAttnError):
+        tsp.bwd(qd, kd, vd, out, lse, dout, D=4, rank=1, dk=torch.empty_like(k))
+    with pytest.raises(tsp.TspAttnError):
+        tsp.ulysses_pack_heads(qd, 2, out=torch.empty(2, 1, 128, 2, 64, dtype=torch.bfloat16))
+    a = torch.zeros(64, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(tsp.TspAttnError):
+        tsp.gemm_nt(a, a, out=torch.empty(64, 64, dtype=torch.float16, device=DEV))
+    with pytest.raises(tsp.TspAttnError):
+        tsp.gemm_nt(a, a, out=torch.empty(64, 64, dtype=torch.bfloat16, device=DEV), accumulate=True)
+    with pytest.raises(tsp.TspAttnError):
+        tsp.gemm_nt(a, a, out=torch.empty(64, 64, dtype=torch.float32))
+    torch.cuda.synchronize()
