@@ -558,18 +558,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dq_bf16_kernel(TspBwdPa
       }
     };
 
-    __syncthreads();  // the previous tile's readers are done with every slot
-#pragma unroll 1
-    for (int s = 0; s < PD; ++s) issue(s);
-#pragma unroll 1
-    for (int t = 0; t < n_steps; ++t) {
+    // Step t: wait for its stage, barrier, load the stage PD ahead, then S^T = K Q^T and
+    // dP^T = V dO^T (lane holds query `col`, keys 8(e/4) + 4*half + e%4), dS^T, and
+    // dQ^T += K^T dS^T (rows = dims, columns = queries). MASK: the step reaches past some
+    // row's position; the unmasked steps come first and run in their own loop, so they
+    // carry no compare or select. Waves whose rows see none of a step's keys only take
+    // part in its barrier.
+    auto run = [&](int t, auto mask_const) {
+      constexpr bool MASK = decltype(mask_const)::value;
       tsp_wait_vm<VM_STAGE * (PD - 1)>();
       __syncthreads();
       issue(t + PD);
-      if (!wave_active || t * BK > wave_max_pos) continue;  // this wave's rows see none of it
+      if (!wave_active || t * BK > wave_max_pos) return;
 
       const uint8_t* st8 = smem + (t % NBUF) * T::STAGE_BYTES;
-      // S^T = K Q^T and dP^T = V dO^T: lane holds query `col`, keys 8(e/4) + 4*half + e%4
       tsp_f32x16 sT, dpT;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -587,18 +589,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dq_bf16_kernel(TspBwdPa
         dpT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[kk], dpT, 0, 0, 0);
       }
       float dsw[16];
-      const bool need_mask = t >= t_mask;
       const int32_t hi = qpos - t * BK - 4 * half;  // key offset limit of this lane
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float pv = tsp_exp2(fmaf(sT[e], p.scale_log2, -lse2));
-        if (need_mask && 8 * (e >> 2) + (e & 3) > hi) pv = 0.f;
+        if constexpr (MASK) {
+          if (8 * (e >> 2) + (e & 3) > hi) pv = 0.f;
+        }
         dsw[e] = pv * (dpT[e] - delta);
       }
       tsp_bf16x8 dsf[2];
       dsf[0] = tsp_pack8(dsw);
       dsf[1] = tsp_pack8(dsw + 8);
-      // dQ^T += K^T dS^T: rows = dims, columns = queries
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -607,7 +609,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dq_bf16_kernel(TspBwdPa
           const tsp_bf16x8 kT = tsp_tr_read8(st8 + tlo[db] + ro, st8 + thi[db] + ro);
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsf[st], acc[db], 0, 0, 0);
         }
-    }
+    };
+
+    __syncthreads();  // the previous tile's readers are done with every slot
+#pragma unroll 1
+    for (int s = 0; s < PD; ++s) issue(s);
+    const int t_split = min(t_mask, n_steps);
+    int t = 0;
+#pragma unroll 1
+    for (; t < t_split; ++t) run(t, std::false_type{});
+#pragma unroll 1
+    for (; t < n_steps; ++t) run(t, std::true_type{});
     tsp_wait_vm<0>();  // trailing duplicate loads land before the slots are reused
 
     if (wave_active && rvalid) {
