@@ -122,6 +122,22 @@ def test_workload_sampled_rows_match_oracle(wr):
     check(out[:, rows], lse[:, :, rows], ref_out, ref_lse, w.torch_dtype(), C=w.C, rows=rows)
 
 
+@pytest.mark.parametrize("rank", range(8))
+def test_every_rank_of_the_7b_shard(rank):
+    """Each of the 8 ranks of the 7B-dense shard at full size (its own queries, the shared
+    K/V): rows at both ends of both chunks and seeded random rows, all 32 heads."""
+    w = workloads.BY_NAME["tsp_7b_shard_s32k"]
+    _note(f"7B shard rank {rank}")
+    q, k, v = workloads.make_inputs(w, rank)
+    out, lse = run(q, k, v, w.D, rank)
+    C = w.C
+    rng = np.random.default_rng(100 + rank)
+    rows = np.unique(np.concatenate([[0, 1, C - 2, C - 1, C, C + 1, 2 * C - 2, 2 * C - 1],
+                                     rng.integers(0, 2 * C, 16)]))
+    ref_out, ref_lse = oracle.causal_attention(q, k, v, w.D, rank, rows=rows, block=64)
+    check(out[:, rows], lse[:, :, rows], ref_out, ref_lse, torch.bfloat16, C=C, rows=rows)
+
+
 # -- the zigzag map ---------------------------------------------------------------------
 
 @pytest.mark.parametrize("S,D,r", [(512, 4, 1), (32768, 8, 3), (262144, 8, 0), (262144, 8, 7), (131072, 1, 0),
