@@ -134,7 +134,8 @@ int tsp_attn_merge(const void* out_a, const float* lse_a, const void* out_b, con
  *             get 0.
  *   delta     device, [B, Hq, 2C] float32 (written): dout_i . out_i per row and head
  * dtype TSP_BF16 or TSP_F32 (fp32 throughout; meant for small shards); bf16 outputs are
- * the fp32 results rounded to nearest even. Same size rules as tsp_attn_fwd plus Hq * dh <= 2^22; all
+ * the fp32 results rounded to nearest even. Same size rules as tsp_attn_fwd plus
+ * Hq * dh <= 2^22; all
  * pointers non-NULL and 16-byte aligned, outputs not overlapping the inputs or each
  * other. Enqueued on `stream`; returns TSP_OK, TSP_EINVAL, TSP_EUNSUPPORTED or
  * TSP_ELAUNCH.
