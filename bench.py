@@ -279,10 +279,13 @@ def main():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--chunk-pipeline", nargs="?", const="fused", choices=["fused", "merge"], default=None,
+    ap.add_argument("--chunk-pipeline", nargs="?", const="fused", choices=["fused", "merge", "pairs"],
+                    default=None,
                     help="time the chunk-pipelined form instead: one key-range launch per gathered "
                          "chunk (2D of them, in ring arrival order), folded into the running result "
-                         "in the kernel's epilogue (fused, the default) or by a separate merge launch")
+                         "in the kernel's epilogue (fused, the default) or by a separate merge launch; "
+                         "pairs: one two-range launch per ring step (D of them, a peer's two chunks "
+                         "each), folded in the epilogue")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward instead (tsp_attn_bwd: delta, dQ and dK/dV kernels) on the "
                          "forward's out / lse; FLOPs counted as 5 products of 2*dh per visible pair")
@@ -344,9 +347,11 @@ def main():
     stream = torch.cuda.Stream(dev)  # default priority
     torch.cuda.synchronize()
 
-    # ring arrival order of the 2D gathered chunks: the rank's own pair first
-    chunks = sorted(range(2 * w.D), key=lambda c: ((c % w.D - rank) % w.D, c))
-    bounds = [(c * w.C, (c + 1) * w.C) for c in chunks]
+    # ring arrival order of the gathered chunks: the rank's own pair first, then the pair
+    # (p, 2D-1-p) of peer p = rank-1, rank-2, ... (mod D)
+    pairs = [((p * w.C, (p + 1) * w.C), ((2 * w.D - 1 - p) * w.C, (2 * w.D - p) * w.C))
+             for p in ((rank - s) % w.D for s in range(w.D))]
+    bounds = [rng for pair in pairs for rng in pair]
     part_o, part_l = torch.empty_like(out), torch.empty_like(lse)
 
     if args.backward:
@@ -362,6 +367,13 @@ def main():
             return
         if not args.chunk_pipeline:
             tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream)
+            return
+        if args.chunk_pipeline == "pairs":
+            tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream, kv_range=pairs[0][0],
+                    kv_range2=pairs[0][1])
+            for ra, rb in pairs[1:]:
+                tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream, kv_range=ra,
+                        kv_range2=rb, accumulate=True)
             return
         tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream, kv_range=bounds[0])
         for rng in bounds[1:]:
@@ -422,6 +434,8 @@ def main():
                      "single launch" if not args.chunk_pipeline else
                      f"chunk pipeline: {len(bounds)} key-range launches, merged in the epilogue"
                      if args.chunk_pipeline == "fused" else
+                     f"chunk pipeline: {len(pairs)} two-range launches (a peer's two chunks each), merged "
+                     "in the epilogue" if args.chunk_pipeline == "pairs" else
                      f"chunk pipeline: {len(bounds)} key-range launches + {len(bounds) - 1} merge launches"),
         },
         "roofline": {

@@ -101,6 +101,22 @@ int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_fu
                        int dtype, void* stream);
 
 /*
+ * tsp_attn_fwd_range2 -- tsp_attn_fwd_range over the union of two key ranges
+ * [kv_begin, kv_end) and [kv_begin2, kv_end2), kv_end <= kv_begin2 <= kv_end2 <= S_total
+ * (an empty second range reduces to tsp_attn_fwd_range): the two chunks a rank receives
+ * from one peer in a step of the zigzag all-gather (chunks r' and 2D-1-r') are taken in
+ * one launch, with one merge into the running result when accumulate = 1. bf16 sweeps
+ * both ranges in one kernel (the running max, sum and output carry from the first range
+ * to the second); fp32 runs one launch per range. Same arguments, layouts, ownership and
+ * errors as tsp_attn_fwd_range, plus TSP_EINVAL for a second range that is not ordered
+ * after the first or not inside [0, S_total].
+ */
+int tsp_attn_fwd_range2(const void* q_local, const void* k_full, const void* v_full, void* out,
+                        float* lse, int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq,
+                        int64_t Hkv, int64_t dh, int64_t kv_begin, int64_t kv_end,
+                        int64_t kv_begin2, int64_t kv_end2, int accumulate, int dtype, void* stream);
+
+/*
  * tsp_attn_merge -- combine two partial results over disjoint key sets:
  *   lse = log(exp(lse_a) + exp(lse_b)),
  *   out = exp(lse_a - lse) * out_a + exp(lse_b - lse) * out_b,

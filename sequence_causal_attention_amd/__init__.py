@@ -39,6 +39,8 @@ SIGNATURES = {
                                     ctypes.c_int, _VP]),
     "tsp_attn_fwd_range": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                           _I64, _I64, ctypes.c_int, ctypes.c_int, _VP]),
+    "tsp_attn_fwd_range2": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                           _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int, _VP]),
     "tsp_attn_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "tsp_attn_bwd": (ctypes.c_int, [_VP] * 10 + [_I64] * 7 + [ctypes.c_int, _VP]),
     "tsp_gemm_bf16_nt": (ctypes.c_int, [_VP, _VP, _VP] + [_I64] * 6 + [ctypes.c_int, _VP]),
@@ -107,7 +109,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D: int, rank: int,
         out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None, kv_range=None,
-        accumulate: bool = False):
+        kv_range2=None, accumulate: bool = False):
     """Causal attention of this rank's zigzag queries against the full K/V.
 
     q_local [B, 2C, Hq, dh], k_full / v_full [B, S_total, Hkv, dh]: contiguous, same
@@ -116,7 +118,8 @@ def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D:
     ``kv_range=(begin, end)`` restricts the keys (tsp_attn_fwd_range): rows without a
     visible key in the range get out = 0, lse = -inf. With ``accumulate=True`` the
     partial over the range is merged into the ``out`` / ``lse`` passed in (a result over
-    disjoint keys) instead of overwriting them.
+    disjoint keys) instead of overwriting them. ``kv_range2=(begin2, end2)``, after
+    ``kv_range``, adds a second key range to the same call (tsp_attn_fwd_range2).
     The call is asynchronous on ``stream`` (default: the current stream).
     """
     for name, t in (("q_local", q_local), ("k_full", k_full), ("v_full", v_full)):
@@ -153,9 +156,15 @@ def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D:
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     lo, hi = (0, S_total) if kv_range is None else (int(kv_range[0]), int(kv_range[1]))
     with torch.cuda.device(q_local.device):
-        st = lib().tsp_attn_fwd_range(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
-                                      lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, lo, hi, int(bool(accumulate)),
-                                      code, handle)
+        if kv_range2 is None:
+            st = lib().tsp_attn_fwd_range(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
+                                          lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, lo, hi,
+                                          int(bool(accumulate)), code, handle)
+        else:
+            lo2, hi2 = int(kv_range2[0]), int(kv_range2[1])
+            st = lib().tsp_attn_fwd_range2(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
+                                           lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, lo, hi, lo2, hi2,
+                                           int(bool(accumulate)), code, handle)
     _check(st)
     return out, lse
 

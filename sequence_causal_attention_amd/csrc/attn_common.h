@@ -33,6 +33,7 @@ struct TspParams {
   int32_t n_hgroups;     // grp / GH
   int32_t n_units;       // B * Hkv * n_hgroups * n_pairs workgroups
   int32_t kv_lo, kv_hi;  // only keys in [kv_lo, kv_hi) take part (whole sequence: 0, S_total)
+  int32_t kv_lo2, kv_hi2;  // and, when kv_hi2 > kv_lo2, the keys in [kv_lo2, kv_hi2) (after kv_hi)
   int32_t accumulate;    // 0: write (out, lse); 1: merge into the (out, lse) already there
   int64_t kv_stride;     // elements between consecutive keys of k / v (Hkv * dh when dense)
   float scale_log2;      // log2(e) / sqrt(dh): scores go straight to the exp2 domain

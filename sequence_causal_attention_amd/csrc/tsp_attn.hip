@@ -92,9 +92,12 @@ int plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_
 template <int DH>
 void launch_bf16(const TspParams& p, hipStream_t stream) {
   using C = Bf16Cfg<DH>;
-  hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::SPS, C::OCC>), dim3(p.n_units),
-                     dim3(C::NW * 64),
-                     0, stream, p);
+  if (p.kv_hi2 > p.kv_lo2)  // two key ranges in one sweep
+    hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::SPS, C::OCC, 2>), dim3(p.n_units),
+                       dim3(C::NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::SPS, C::OCC, 1>), dim3(p.n_units),
+                       dim3(C::NW * 64), 0, stream, p);
 }
 
 template <int DH>
@@ -178,9 +181,10 @@ int attn_launch(const TspParams& p, int64_t dh, int dtype, hipStream_t stream) {
 
 extern "C" {
 
-int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse,
-                       int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh,
-                       int64_t kv_begin, int64_t kv_end, int accumulate, int dtype, void* stream) {
+int tsp_attn_fwd_range2(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse,
+                        int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh,
+                        int64_t kv_begin, int64_t kv_end, int64_t kv_begin2, int64_t kv_end2, int accumulate,
+                        int dtype, void* stream) {
   if (!q_local || !k_full || !v_full || !out || !lse) return fail(TSP_EINVAL, "null pointer argument");
   if (!aligned16(q_local) || !aligned16(k_full) || !aligned16(v_full) || !aligned16(out) || !aligned16(lse))
     return fail(TSP_EINVAL, "pointers must be 16-byte aligned");
@@ -191,7 +195,11 @@ int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_fu
   if (kv_begin < 0 || kv_begin > kv_end || kv_end > S_total)
     return fail(TSP_EINVAL, "key range [%lld, %lld) not inside [0, %lld]", (long long)kv_begin,
                 (long long)kv_end, (long long)S_total);
+  if (kv_begin2 > kv_end2 || kv_end2 > S_total || (kv_end2 > kv_begin2 && kv_begin2 < kv_end))
+    return fail(TSP_EINVAL, "second key range [%lld, %lld) must lie inside [%lld, %lld]", (long long)kv_begin2,
+                (long long)kv_end2, (long long)kv_end, (long long)S_total);
   if (accumulate != 0 && accumulate != 1) return fail(TSP_EINVAL, "accumulate must be 0 or 1");
+  const bool two = kv_end2 > kv_begin2;
   p.kv_lo = (int32_t)kv_begin;
   p.kv_hi = (int32_t)kv_end;
   p.accumulate = accumulate;
@@ -203,21 +211,40 @@ int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_fu
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
   if (dtype == TSP_BF16) {
+    if (two) {  // one sweep over both ranges
+      p.kv_lo2 = (int32_t)kv_begin2;
+      p.kv_hi2 = (int32_t)kv_end2;
+    }
     switch (dh) {
       case 64: launch_bf16<64>(p, s); break;
       case 128: launch_bf16<128>(p, s); break;
       case 256: launch_bf16<256>(p, s); break;
     }
   } else {
-    switch (dh) {
-      case 64: launch_f32<64>(p, s); break;
-      case 128: launch_f32<128>(p, s); break;
-      case 256: launch_f32<256>(p, s); break;
+    // fp32: one launch per range, the second merged into the first's result
+    for (int rg = 0; rg < (two ? 2 : 1); ++rg) {
+      if (rg == 1) {
+        p.kv_lo = (int32_t)kv_begin2;
+        p.kv_hi = (int32_t)kv_end2;
+        p.accumulate = 1;
+      }
+      switch (dh) {
+        case 64: launch_f32<64>(p, s); break;
+        case 128: launch_f32<128>(p, s); break;
+        case 256: launch_f32<256>(p, s); break;
+      }
     }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TSP_ELAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return tsp_host::ok();
+}
+
+int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse,
+                       int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh,
+                       int64_t kv_begin, int64_t kv_end, int accumulate, int dtype, void* stream) {
+  return tsp_attn_fwd_range2(q_local, k_full, v_full, out, lse, B, S_total, D, rank, Hq, Hkv, dh, kv_begin, kv_end,
+                             S_total, S_total, accumulate, dtype, stream);
 }
 
 int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse, int64_t B,

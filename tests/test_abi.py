@@ -140,6 +140,20 @@ def test_range_outside_sequence_rejected(lib, lo, hi):
     assert "range" in lib.tsp_attn_last_error().decode()
 
 
+@pytest.mark.parametrize("r1,r2", [
+    ((0, 128), (64, 256)),    # overlapping
+    ((256, 384), (0, 128)),   # second before the first
+    ((0, 128), (256, 600)),   # second past S_total
+    ((0, 128), (300, 200)),   # second reversed
+])
+def test_second_range_must_follow_the_first(lib, r1, r2):
+    f = _fake()
+    a = VALID
+    assert lib.tsp_attn_fwd_range2(f, f, f, f, f, a["B"], a["S_total"], a["D"], a["rank"], a["Hq"], a["Hkv"],
+                                   a["dh"], *r1, *r2, 0, a["dtype"], None) == tsp.TSP_EINVAL
+    assert "second key range" in lib.tsp_attn_last_error().decode()
+
+
 def test_range_shares_fwd_validation(lib):
     f = _fake()
     assert lib.tsp_attn_fwd_range(f, f, f, f, None, 1, 512, 4, 1, 4, 1, 64, 0, 512, 0, tsp.TSP_F32, None) == \

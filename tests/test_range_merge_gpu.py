@@ -129,8 +129,8 @@ PIPE_CASES = [  # (B, S_total, D, rank, Hq, Hkv, dh, dtype, order)
 def _bounds(S, D, r, order):
     C = S // (2 * D)
     chunks = list(range(2 * D))
-    if order == "ring":  # own chunks first, then the others as a ring all-gather delivers them
-        chunks = sorted(chunks, key=lambda c: ((c % D - r) % D, c))
+    if order == "ring":  # own pair first, then the pair (p, 2D-1-p) of peer p = r-1, r-2, ...
+        chunks = [c for p in ((r - s) % D for s in range(D)) for c in (p, 2 * D - 1 - p)]
     elif order == "reverse":
         chunks = chunks[::-1]
     return [(c * C, (c + 1) * C) for c in chunks]
@@ -284,6 +284,146 @@ def test_range_invalid_arguments_write_nothing():
     for lo, hi in [(10, 9), (-1, 5), (0, 513), (600, 700)]:
         with pytest.raises(tsp.TspAttnError) as ei:
             tsp.fwd(qd, kd, vd, D=4, rank=1, kv_range=(lo, hi), out=out, lse=lse)
+        assert ei.value.status == tsp.TSP_EINVAL
+    torch.cuda.synchronize()
+    assert (out == 5).all() and (lse == 5).all()
+
+
+RANGE2_CASES = [  # (B, S_total, D, rank, Hq, Hkv, dh, dtype, first range, second range)
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, (128, 256), (1792, 1920)),   # peer 1's two chunks
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, (384, 512), (1536, 1664)),   # own two chunks
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, (100, 700), (700, 1800)),    # adjacent, unaligned
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, (1900, 2000), (2000, 2048)),  # empty for every row
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, (0, 60), (1600, 1700)),      # second: 2nd chunk only
+    (1, 2048, 8, 0, 4, 4, 128, torch.bfloat16, (33, 95), (95, 95)),         # empty second range
+    (1, 2048, 8, 0, 4, 4, 128, torch.bfloat16, (33, 33), (60, 1000)),       # empty first range
+    (1, 2048, 8, 0, 4, 4, 128, torch.bfloat16, (1, 2), (40, 41)),           # one key each
+    (1, 4096, 4, 2, 12, 2, 256, torch.bfloat16, (512, 1024), (3072, 3584)),  # GQA, dh 256
+    (1, 1024, 2, 1, 8, 2, 64, torch.bfloat16, (256, 512), (512, 768)),      # dh 64
+    (1, 1200, 3, 2, 6, 2, 128, torch.bfloat16, (0, 200), (1000, 1200)),     # ragged chunks
+    (2, 1024, 4, 1, 4, 2, 128, torch.bfloat16, (128, 256), (768, 896)),     # batch of 2
+    (1, 4096, 1, 0, 4, 4, 128, torch.bfloat16, (17, 1000), (2000, 3001)),   # D = 1
+    (1, 512, 4, 1, 4, 1, 64, torch.float32, (0, 64), (448, 512)),           # fp32
+    (1, 600, 3, 1, 2, 1, 128, torch.float32, (37, 100), (451, 600)),        # fp32 ragged
+]
+
+
+def _base_range(S, lo, hi2):
+    """Keys outside both ranges, for the running result that an accumulating call adds to."""
+    return (hi2, S) if hi2 < S else (0, lo)
+
+
+@pytest.mark.parametrize("accumulate", [False, True], ids=["write", "accumulate"])
+@pytest.mark.parametrize("case", RANGE2_CASES, ids=lambda c: "B{}_S{}_D{}_r{}_d{}_{}_{}_{}".format(
+    *c[:4], c[6], str(c[7])[6:], *c[8:]))
+def test_two_ranges_match_oracle_merge(case, accumulate):
+    """One call over two key ranges equals the oracle's merge of the two range partials
+    (and, accumulating, of those and the running result's range)."""
+    B, S, D, r, Hq, Hkv, dh, dtype, ra, rb = case
+    _note(f"two ranges {case} accumulate={accumulate}")
+    q, k, v = workloads.make_custom(B, S, D, Hq, Hkv, dh, dtype, seed=41)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    oa, la = oracle.causal_attention_range(q, k, v, D, r, *ra)
+    ob, lb = oracle.causal_attention_range(q, k, v, D, r, *rb)
+    ref_o, ref_l = oracle.merge_partials(oa, la, ob, lb)
+    if accumulate:
+        base = _base_range(S, ra[0], rb[1])
+        o, l = tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=base)
+        tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=ra, kv_range2=rb, out=o, lse=l, accumulate=True)
+        oc, lc = oracle.causal_attention_range(q, k, v, D, r, *base)
+        ref_o, ref_l = oracle.merge_partials(oc, lc, ref_o, ref_l)
+    else:
+        o, l = tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=ra, kv_range2=rb)
+    torch.cuda.synchronize()
+    check_partial(_np(o), _np(l), ref_o, ref_l, dtype)
+
+
+def test_two_ranges_covering_all_keys_match_fwd():
+    """Two ranges that split the keys give the single launch's result to rounding."""
+    _note("two ranges == fwd")
+    q, k, v = workloads.make_custom(1, 2048, 8, 4, 4, 128, torch.bfloat16, seed=5)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o1, l1 = tsp.fwd(qd, kd, vd, D=8, rank=3)
+    o2, l2 = tsp.fwd(qd, kd, vd, D=8, rank=3, kv_range=(0, 1000), kv_range2=(1000, 2048))
+    torch.cuda.synchronize()
+    # the same sweep over the same keys: only the stage boundary at 1000 differs
+    assert (o1.float() - o2.float()).abs().max().item() <= TOL[torch.bfloat16]
+    assert (l1 - l2).abs().max().item() <= 2.0 ** -8
+
+
+def _pair_pipeline(qd, kd, vd, D, r, C):
+    """One call per step of a ring all-gather: the rank's own two chunks first, then the
+    two chunks of each peer (r-1, r-2, ... mod D) in arrival order, accumulated."""
+    acc_o = acc_l = None
+    for s in range(D):
+        p = (r - s) % D
+        ra, rb = (p * C, (p + 1) * C), ((2 * D - 1 - p) * C, (2 * D - p) * C)
+        if acc_o is None:
+            acc_o, acc_l = tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=ra, kv_range2=rb)
+        else:
+            tsp.fwd(qd, kd, vd, D=D, rank=r, kv_range=ra, kv_range2=rb, out=acc_o, lse=acc_l, accumulate=True)
+    torch.cuda.synchronize()
+    return acc_o, acc_l
+
+
+PAIR_CASES = [  # (B, S_total, D, rank, Hq, Hkv, dh, dtype)
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16),
+    (1, 2048, 8, 0, 4, 4, 128, torch.bfloat16),
+    (1, 2048, 8, 7, 4, 4, 128, torch.bfloat16),
+    (1, 4096, 4, 2, 12, 2, 256, torch.bfloat16),
+    (1, 1024, 2, 1, 8, 2, 64, torch.bfloat16),
+    (1, 1200, 3, 2, 6, 2, 128, torch.bfloat16),   # ragged: chunks of 200 keys
+    (1, 512, 4, 1, 4, 1, 64, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=lambda c: "B{}_S{}_D{}_r{}_H{}x{}_d{}_{}".format(
+    *c[:7], str(c[7])[6:]))
+def test_ring_pair_pipeline(case):
+    B, S, D, r, Hq, Hkv, dh, dtype = case
+    _note(f"pair pipeline {case}")
+    q, k, v = workloads.make_custom(B, S, D, Hq, Hkv, dh, dtype, seed=43)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, l = _pair_pipeline(qd, kd, vd, D, r, S // (2 * D))
+    ref_out, ref_lse = oracle.causal_attention(q, k, v, D, r)
+    out, lse = _np(o), _np(l)
+    assert np.isfinite(lse).all()
+    check_partial(out, lse, ref_out, ref_lse, dtype)
+    of, lf = tsp.fwd(qd, kd, vd, D=D, rank=r)
+    torch.cuda.synchronize()
+    assert np.abs(out - _np(of)).max() <= TOL[dtype]
+    assert np.abs(lse - _np(lf)).max() <= (2.0 ** -8 if dtype == torch.bfloat16 else 1e-5)
+
+
+def test_ring_pair_pipeline_workload_sampled():
+    """The 7B shard at its full size, one call per ring step, on sampled rows."""
+    w = workloads.BY_NAME["tsp_7b_shard_s32k"]
+    r = w.ranks[0]
+    _note(f"pair pipeline workload {w.name} rank {r}")
+    q, k, v = workloads.make_inputs(w, r)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    C = w.S_total // (2 * w.D)
+    o, l = _pair_pipeline(qd, kd, vd, w.D, r, C)
+    rows = np.concatenate([np.arange(0, 48), np.arange(C - 16, C + 32), np.arange(2 * C - 16, 2 * C)])
+    heads = [0, 17, 31]
+    ref_out, ref_lse = oracle.causal_attention(q, k, v, w.D, r, rows=rows, heads=heads)
+    idx = torch.as_tensor(rows, device=DEV)
+    hidx = torch.as_tensor(heads, device=DEV)
+    out = _np(o.index_select(1, idx).index_select(2, hidx))
+    lse = _np(l.index_select(1, hidx).index_select(2, idx))
+    check_partial(out, lse, ref_out, ref_lse, w.torch_dtype())
+
+
+def test_two_ranges_invalid_write_nothing():
+    _note("two ranges invalid")
+    q, k, v = workloads.make_custom(1, 512, 4, 4, 1, 64, torch.bfloat16, seed=3)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.full_like(qd, 5.0)
+    lse = torch.full((1, 4, 128), 5.0, device=DEV)
+    for ra, rb in [((0, 100), (50, 200)), ((0, 100), (300, 200)), ((0, 100), (400, 513)),
+                   ((100, 200), (0, 50))]:
+        with pytest.raises(tsp.TspAttnError) as ei:
+            tsp.fwd(qd, kd, vd, D=4, rank=1, kv_range=ra, kv_range2=rb, out=out, lse=lse)
         assert ei.value.status == tsp.TSP_EINVAL
     torch.cuda.synchronize()
     assert (out == 5).all() and (lse == 5).all()
