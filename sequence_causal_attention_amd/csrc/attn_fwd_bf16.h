@@ -137,7 +137,8 @@ struct Bf16Stage {
 };
 
 // NR: key ranges of the launch, 1 ([kv_lo, kv_hi)) or 2 (also [kv_lo2, kv_hi2), after the
-// first): the running max, sum and output carry over from one range's sweep to the next.
+// first): one sweep runs through both, the second range's stages following the first's in
+// the LDS ring, so the pipeline neither drains nor refills between them.
 template <int DH, int NW, int RB, int NBUF, int SPS, int OCC, int NR>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p) {
   using St = Bf16Stage<DH, NW, NBUF, SPS>;
@@ -287,255 +288,324 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
         for (int e = 0; e < 16; ++e) acc[rb][db][e] = 0.f;
     }
 
-    // ---- the sweep over one key range [r_lo, r_hi) ---------------------------------------
-    auto sweep = [&](const int32_t r_lo, const int32_t r_hi) {
-      // The sweep starts at the stage boundary at or below r_lo; key indices below are
-      // relative to it (keys in [kv_base, r_lo) are loaded but masked).
-      const int32_t kv_base = (r_lo / St::BKS) * St::BKS;
-      const int32_t kv_lo_rel = r_lo - kv_base;
-      // relative end of the keys this tile sweeps: its last position, or the range end
-      const int32_t kv_end = min(r_hi, tile_end) - kv_base;
-      if (kv_end <= kv_lo_rel) return;  // nothing of this range is visible to the tile
-      const uint16_t* __restrict__ kbase = kg + ((int64_t)b * p.S_total + kv_base) * p.kv_stride + (int64_t)hk * DH;
-      const uint16_t* __restrict__ vbase = vg + ((int64_t)b * p.S_total + kv_base) * p.kv_stride + (int64_t)hk * DH;
-      const int32_t n_kv = (kv_end + BK - 1) / BK;             // pipeline steps
-      const int32_t n_stage = (kv_end + St::BKS - 1) / St::BKS;  // stages
-      // last visible key of each row: its position, or the range end if that comes first
-      int32_t qpos[RB];
+    // ---- the keys of the sweep --------------------------------------------------------
+    // The sweep starts at the stage boundary at or below kv_lo; key indices below are
+    // relative to it (keys in [kv_base, kv_lo) are loaded but masked).
+    const int32_t kv_base = (p.kv_lo / St::BKS) * St::BKS;
+    const int32_t kv_lo_rel = p.kv_lo - kv_base;
+    // relative end of the keys this tile sweeps: its last position, or the range end
+    const int32_t kv_end = min(p.kv_hi, tile_end) - kv_base;
+    const uint16_t* __restrict__ kbase = kg + ((int64_t)b * p.S_total + kv_base) * p.kv_stride + (int64_t)hk * DH;
+    const uint16_t* __restrict__ vbase = vg + ((int64_t)b * p.S_total + kv_base) * p.kv_stride + (int64_t)hk * DH;
+    int32_t n_kv1 = (kv_end + BK - 1) / BK;             // pipeline steps
+    int32_t n_stage1 = (kv_end + St::BKS - 1) / St::BKS;  // stages
+    // last visible key of each row: its position, or the range end if that comes first
+    int32_t qpos[RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) qpos[rb] = min(pos[rb], r_hi - 1);
-      // steps [u_left, t_mask) are visible to every row of the wave; earlier steps hold
-      // keys below r_lo, later ones keys past some row's position or the range end
-      const int32_t t_mask = min(n_kv, max(0, min(wave_min_pos + 1, r_hi) - kv_base) / BK);
-      const int32_t u_left = (kv_lo_rel + BK - 1) / BK;
+    for (int rb = 0; rb < RB; ++rb) qpos[rb] = min(pos[rb], p.kv_hi - 1);
+    // steps [u_left, t_mask) are visible to every row of the wave; earlier steps hold keys
+    // below kv_lo, later ones keys past some row's position or the range end: all masked
+    int32_t t_mask = min(n_kv1, max(0, min(wave_min_pos + 1, p.kv_hi) - kv_base) / BK);
+    const int32_t u_left = (kv_lo_rel + BK - 1) / BK;
+    // The second range (two-range launches): its stages follow the first range's whole
+    // stages in the ring and its steps start at step T1; its keys are indexed from its own
+    // stage-aligned start kv_base2. A tile that sees a key of it also sees the first range,
+    // which lies below (an unseen first range is dropped all the same).
+    int32_t T1 = n_kv1, n_kv2 = 0, n_stage2 = 0;
+    int32_t kv_base2 = 0, kv_lo_rel2 = 0, kv_end2 = 0, t_mask2 = 0, u_left2 = 0;
+    int32_t qpos2[RB];
+    const uint16_t* __restrict__ kbase2 = kbase;
+    const uint16_t* __restrict__ vbase2 = vbase;
+    bool run_on = false;  // the unmasked steps run on from the first range into the second
+    if constexpr (NR == 2) {
+      int32_t n_full1 = kv_end / St::BKS;
+      if (kv_end <= kv_lo_rel) n_kv1 = n_stage1 = t_mask = n_full1 = T1 = 0;
+      kv_base2 = (p.kv_lo2 / St::BKS) * St::BKS;
+      kv_lo_rel2 = p.kv_lo2 - kv_base2;
+      kv_end2 = min(p.kv_hi2, tile_end) - kv_base2;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) qpos2[rb] = min(pos[rb], p.kv_hi2 - 1);
+      if (kv_end2 > kv_lo_rel2) {
+        T1 = n_stage1 * SPS;  // the first range's steps, padded to whole stages
+        n_kv2 = (kv_end2 + BK - 1) / BK;
+        n_stage2 = (kv_end2 + St::BKS - 1) / St::BKS;
+        t_mask2 = min(n_kv2, max(0, min(wave_min_pos + 1, p.kv_hi2) - kv_base2) / BK);
+        u_left2 = (kv_lo_rel2 + BK - 1) / BK;
+        kbase2 = kg + ((int64_t)b * p.S_total + kv_base2) * p.kv_stride + (int64_t)hk * DH;
+        vbase2 = vg + ((int64_t)b * p.S_total + kv_base2) * p.kv_stride + (int64_t)hk * DH;
+        run_on = n_full1 == n_stage1 && t_mask == T1 && u_left2 == 0;
+      }
+    }
+    const int64_t stage_off2 = (int64_t)n_stage1 * stage_stride;  // offset of the second range's stages
+    const int32_t n_kv = T1 + n_kv2;              // pipeline steps of both ranges
+    const int32_t n_stage = n_stage1 + n_stage2;  // stages of both ranges
 
-      // ---- stage loads: global -> LDS, this wave's share --------------------------------
-      // Any stage: rows past the tile's last position are clamped to it (never read past it).
-      auto issue_stage = [&](int s) {
-        const int32_t kv0 = s * St::BKS;
-        const uint32_t base = smem_addr + (s % NBUF) * St::SLOT_STRIDE;
-#pragma unroll
-        for (int q = 0; q < St::LPW; ++q) {
-          const int32_t over = max(0, kv0 + dma_row[q] - (kv_end - 1));  // rows beyond the last key
-          const uint16_t* tb = (dma_isv[q] ? vbase : kbase) + (int64_t)kv0 * kv_row_stride;
-          tsp_lds_dma16(tb, dma_voff[q] - (uint32_t)(over * row_bytes_g), base + dma_slot[q]);
+    // ---- stage loads: global -> LDS, this wave's share --------------------------------
+    // Any stage: rows past the tile's last position (or its range's end) are clamped to it
+    // (never read past it).
+    auto issue_stage = [&](int s) {
+      const uint16_t* kb = kbase;
+      const uint16_t* vb = vbase;
+      int32_t kv0 = s * St::BKS, end = kv_end;
+      if constexpr (NR == 2) {
+        if (s >= n_stage1) {  // a stage of the second range
+          kb = kbase2;
+          vb = vbase2;
+          kv0 = (s - n_stage1) * St::BKS;
+          end = kv_end2;
         }
-      };
-      // Wait until stage s has landed for every wave; the stages issued after it (up to
-      // last_issued) stay in flight.
-      auto stage_ready = [&](int s, int last_issued) {
-        tsp_wait_vmcnt(St::LPW * (last_issued - s));
-        __syncthreads();
-      };
+      }
+      const uint32_t base = smem_addr + (s % NBUF) * St::SLOT_STRIDE;
+#pragma unroll
+      for (int q = 0; q < St::LPW; ++q) {
+        const int32_t over = max(0, kv0 + dma_row[q] - (end - 1));  // rows beyond the last key
+        const uint16_t* tb = (dma_isv[q] ? vb : kb) + (int64_t)kv0 * kv_row_stride;
+        tsp_lds_dma16(tb, dma_voff[q] - (uint32_t)(over * row_bytes_g), base + dma_slot[q]);
+      }
+    };
+    // Wait until stage s has landed for every wave; the stages issued after it (up to
+    // last_issued) stay in flight.
+    auto stage_ready = [&](int s, int last_issued) {
+      tsp_wait_vmcnt(St::LPW * (last_issued - s));
+      __syncthreads();
+    };
 
-      // ---- pipeline pieces ---------------------------------------------------------------
-      // step t reads keys [32t, 32t+32): stage t/SPS, rows 32*(t%SPS) .. of its slot
-      auto qk = [&](int t, tsp_f32x16(&sc)[RB]) {
-        const uint8_t* kt = smem + ((t / SPS) % NBUF) * St::SLOT_STRIDE + (t % SPS) * BK * St::ROW_BYTES;
+    // ---- pipeline pieces ---------------------------------------------------------------
+    // step t reads keys [32t, 32t+32): stage t/SPS, rows 32*(t%SPS) .. of its slot
+    auto qk = [&](int t, tsp_f32x16(&sc)[RB]) {
+      const uint8_t* kt = smem + ((t / SPS) % NBUF) * St::SLOT_STRIDE + (t % SPS) * BK * St::ROW_BYTES;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[rb][e] = 0.f;
+      tsp_bf16x8 kf[NKK];  // all K operands of the step in flight before the first MFMA
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        kf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(kt + koff[kk]));
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) sc[rb][e] = 0.f;
-        tsp_bf16x8 kf[NKK];  // all K operands of the step in flight before the first MFMA
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          kf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(kt + koff[kk]));
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[rb][kk], sc[rb], 0, 0, 0);
-      };
-      // key kv_base + s*BK + 8(e/4) + 4*half + (e%4) of query column `col` is visible iff
-      // it is <= qpos (the query's position, capped below kv_hi) and >= kv_lo
-      auto mask = [&](int s, tsp_f32x16(&sc)[RB]) {
-        const int32_t lo = kv_lo_rel - s * BK - 4 * half;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int32_t hi = qpos[rb] - kv_base - s * BK - 4 * half;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int off = 8 * (e >> 2) + (e & 3);
-            if (off > hi || off < lo) sc[rb][e] = -INFINITY;
-          }
+          sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[rb][kk], sc[rb], 0, 0, 0);
+    };
+    // key kv_base + s*BK + 8(e/4) + 4*half + (e%4) of query column `col` is visible iff
+    // it is <= qpos (the query's position, capped below kv_hi) and >= kv_lo; in the second
+    // range, key kv_base2 + (s - T1)*BK + ... against qpos2 and kv_lo2
+    auto mask = [&](int s, tsp_f32x16(&sc)[RB]) {
+      int32_t lo_rel = kv_lo_rel, base = kv_base, u = s;
+      bool second = false;
+      if constexpr (NR == 2) {
+        second = s >= T1;
+        if (second) {
+          lo_rel = kv_lo_rel2;
+          base = kv_base2;
+          u = s - T1;
         }
-      };
-      auto needs_mask = [&](int s) { return s >= t_mask || s < u_left; };
-      // Row max of a step's scores over this lane's 16 keys (raw score units): the two
-      // halves of a row are tested separately, which decides the same wave-wide ballot as
-      // testing the full row, and the full max is formed only when a rescale is due.
-      auto rowmax = [&](const tsp_f32x16(&sc)[RB], float(&mx)[RB]) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          float m = sc[rb][0];
-#pragma unroll
-          for (int e = 1; e < 16; ++e) m = fmaxf(m, sc[rb][e]);
-          mx[rb] = m;
-        }
-      };
-      auto rescale_needed = [&](const float(&mx)[RB]) {
-        bool need = false;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) need |= mx[rb] > m_thr[rb];
-        return __builtin_amdgcn_ballot_w64(need) != 0;  // wave-uniform
-      };
-      // Raise the running max to cover this step (rare after the first step): scale the
-      // accumulated output and sum by 2^(m_old - m_new).
-      auto rescale = [&](const float(&mx)[RB]) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float m_new = fmaxf(m_run[rb], tsp_max_halves(mx[rb]) * p.scale_log2);
-          m_thr[rb] = (m_new + TSP_RESCALE_SLACK) * inv_scale_log2;
-          // a row with no visible key yet (both -inf) keeps its zero state
-          const float alpha = m_new == -INFINITY ? 1.f : tsp_exp2(m_run[rb] - m_new);
-          m_run[rb] = m_new;
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[rb][db][e] *= alpha;
-        }
-      };
-      // guard: a row may not have seen a visible key yet (m_run = -inf), so use 0 as its
-      // exponent offset; its scores are all -inf and its weights 0
-      auto softmax = [&](const tsp_f32x16(&sc)[RB], tsp_bf16x8(&pf)[RB][2], bool guard) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float mneg = (guard && m_run[rb] == -INFINITY) ? 0.f : -m_run[rb];
-          float lsum = 0.f;
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            float pw[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pw[e] = tsp_exp2(fmaf(sc[rb][st * 8 + e], p.scale_log2, mneg));
-            tsp_u32x4 w;
-            w[0] = tsp_pack_bf16(pw[0], pw[1]);
-            w[1] = tsp_pack_bf16(pw[2], pw[3]);
-            w[2] = tsp_pack_bf16(pw[4], pw[5]);
-            w[3] = tsp_pack_bf16(pw[6], pw[7]);
-            // the row sum uses the rounded weights the PV product applies
-#pragma unroll
-            for (int e = 0; e < 4; ++e) lsum = tsp_sum_bf16_pair(w[e], lsum);
-            pf[rb][st] = __builtin_bit_cast(tsp_bf16x8, w);
-          }
-          l_run[rb] += lsum;
-        }
-      };
-      auto pv = [&](int t, const tsp_bf16x8(&pf)[RB][2]) {
-        const uint8_t* vt =
-            smem + ((t / SPS) % NBUF) * St::SLOT_STRIDE + (t % SPS) * BK * St::ROW_BYTES;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const uint8_t* a = vt + voff[db] + st * 16 * St::ROW_BYTES;
-            const tsp_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a));
-            const tsp_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a + 8 * St::ROW_BYTES));
-            const tsp_bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb][st], acc[rb][db], 0, 0, 0);
-          }
-        }
-      };
-
-      // ---- prologue -------------------------------------------------------------------
-      __syncthreads();  // the previous tile's readers are done with every buffer
-      const int pro = min(PD, n_stage - 1);
-      for (int s = 0; s <= pro; ++s) issue_stage(s);
-      stage_ready(0, pro);
-
-      tsp_f32x16 s_cur[RB];
-      float mx[RB];
-      qk(0, s_cur);
-      if (needs_mask(0)) mask(0, s_cur);
-      rowmax(s_cur, mx);
-
-      // ---- main sweep ----------------------------------------------------------------------
-      // Fast path: steps whose successor needs no mask and whose prefetched stage lies fully
-      // below kv_end. Unrolled over whole ring cycles so every LDS slot is a compile-time
-      // offset and the two score tiles alternate without copies; constant vmcnt; no clamping.
-      constexpr int VM_STEADY = St::LPW * (PD - 1);
-      static_assert(VM_STEADY < 16, "vmcnt immediate");
-      constexpr int GROUP = (NBUF * SPS) % 2 == 0 ? NBUF * SPS : 2 * NBUF * SPS;  // steps per unrolled group
-      const int32_t n_full = kv_end / St::BKS;  // stages with every key below kv_end
-      const int t_fast = u_left == 0 ? min(t_mask - 1, (n_full - PD) * SPS - 1) : 0;
-      tsp_f32x16 s_alt[RB];
-      // Stage boundary: wait until stage NEXT (relative to t0 / SPS) landed for every wave,
-      // then issue the stage PD ahead into the slot two stages back.
-      auto boundary = [&](auto next_const, int t0) {
-        constexpr int NEXT = decltype(next_const)::value;
-        __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // that stage landed (this wave's part)
-        __syncthreads();  // ... for every wave; the slot two stages back is free again
-        const int64_t adv = (int64_t)(t0 / SPS + NEXT + PD) * stage_stride;
-        const uint32_t base = smem_addr + ((NEXT + PD) % NBUF) * St::SLOT_STRIDE;
-#pragma unroll
-        for (int q = 0; q < St::LPW; ++q)
-          tsp_lds_dma16((dma_isv[q] ? vbase : kbase) + adv, dma_voff[q], base + dma_slot[q]);
-      };
-      // LAG (second half of the waves, one of the two waves of each SIMD): the barrier of
-      // stage k comes after the PV products of step SPS*k - 2 instead of before the QK
-      // products of step SPS*k - 1. Every barrier still precedes the first read of its stage
-      // and follows the last read of the stage two back, but the two waves of a SIMD then run
-      // their matrix and vector phases in alternation (one's softmax under the other's MFMAs).
-      auto fast_step = [&](auto u_const, auto lag_const, int t0) {
-        constexpr int U = decltype(u_const)::value;  // step t = t0 + U, t0 a multiple of GROUP
-        constexpr bool LAG = decltype(lag_const)::value;
-        tsp_f32x16(&sc)[RB] = (U % 2 == 0) ? s_cur : s_alt;
-        tsp_f32x16(&sn)[RB] = (U % 2 == 0) ? s_alt : s_cur;
-        if (rescale_needed(mx)) rescale(mx);
-        if constexpr (!LAG && (U + 1) % SPS == 0)  // step t+1 opens a new stage
-          boundary(std::integral_constant<int, (U + 1) / SPS>{}, t0);
-        tsp_bf16x8 pf[RB][2];
-        qk(U + 1, sn);     // matrix pipe: next step's scores
-        softmax(sc, pf, false);  // vector pipe: this step's weights
-        pv(U, pf);         // matrix pipe: this step's output
-        if constexpr (LAG && (U + 2) % SPS == 0)  // the next stage's barrier, one phase early
-          boundary(std::integral_constant<int, (U + 2) / SPS>{}, t0);
-        rowmax(sn, mx);    // vector pipe: next step's row max
-      };
-      auto fast_group = [&]<int... Us>(std::integer_sequence<int, Us...>, auto lag_const, int t0) {
-        (fast_step(std::integral_constant<int, Us>{}, lag_const, t0), ...);
-      };
-      int t = 0;
-      constexpr bool PINGPONG = TSP_PINGPONG && SPS == 2 && NW % 2 == 0;
-      if (PINGPONG && TSP_PP_LAGGED(wave)) {
-        for (; t + GROUP <= t_fast; t += GROUP)
-          fast_group(std::make_integer_sequence<int, GROUP>{}, std::bool_constant<PINGPONG>{}, t);
-      } else {
-        for (; t + GROUP <= t_fast; t += GROUP)
-          fast_group(std::make_integer_sequence<int, GROUP>{}, std::false_type{}, t);
       }
-      int issued = t > 0 ? t / SPS + PD : pro;  // last stage issued so far
-
-      // General path: the masked steps near the diagonal, the partial last stage and the
-      // ring drain.
-      for (; t < n_kv; ++t) {
-        if (rescale_needed(mx)) rescale(mx);
-        tsp_bf16x8 pf[RB][2];
-        if (t + 1 < n_kv) {
-          if ((t + 1) % SPS == 0) {
-            stage_ready((t + 1) / SPS, issued);
-            if (issued + 1 < n_stage) issue_stage(++issued);
-          }
-          qk(t + 1, s_alt);
-          softmax(s_cur, pf, true);
-          pv(t, pf);
-          if (needs_mask(t + 1)) mask(t + 1, s_alt);
-          rowmax(s_alt, mx);
+      const int32_t lo = lo_rel - u * BK - 4 * half;
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_alt[rb];
-        } else {
-          softmax(s_cur, pf, true);
-          pv(t, pf);
+      for (int rb = 0; rb < RB; ++rb) {
+        int32_t last = qpos[rb];
+        if constexpr (NR == 2) last = second ? qpos2[rb] : last;
+        const int32_t hi = last - base - u * BK - 4 * half;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = 8 * (e >> 2) + (e & 3);
+          if (off > hi || off < lo) sc[rb][e] = -INFINITY;
         }
       }
     };
-    if constexpr (NR == 1) {
-      sweep(p.kv_lo, p.kv_hi);
-    } else {  // one sweep body for both ranges (the loop is not unrolled)
-#pragma unroll 1
-      for (int rg = 0; rg < NR; ++rg) sweep(rg == 0 ? p.kv_lo : p.kv_lo2, rg == 0 ? p.kv_hi : p.kv_hi2);
+    auto needs_mask = [&](int s) {
+      if constexpr (NR == 2) {
+        if (s >= T1) return s - T1 >= t_mask2 || s - T1 < u_left2;
+      }
+      return s >= t_mask || s < u_left;
+    };
+    // Row max of a step's scores over this lane's 16 keys (raw score units): the two
+    // halves of a row are tested separately, which decides the same wave-wide ballot as
+    // testing the full row, and the full max is formed only when a rescale is due.
+    auto rowmax = [&](const tsp_f32x16(&sc)[RB], float(&mx)[RB]) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float m = sc[rb][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) m = fmaxf(m, sc[rb][e]);
+        mx[rb] = m;
+      }
+    };
+    auto rescale_needed = [&](const float(&mx)[RB]) {
+      bool need = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) need |= mx[rb] > m_thr[rb];
+      return __builtin_amdgcn_ballot_w64(need) != 0;  // wave-uniform
+    };
+    // Raise the running max to cover this step (rare after the first step): scale the
+    // accumulated output and sum by 2^(m_old - m_new).
+    auto rescale = [&](const float(&mx)[RB]) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float m_new = fmaxf(m_run[rb], tsp_max_halves(mx[rb]) * p.scale_log2);
+        m_thr[rb] = (m_new + TSP_RESCALE_SLACK) * inv_scale_log2;
+        // a row with no visible key yet (both -inf) keeps its zero state
+        const float alpha = m_new == -INFINITY ? 1.f : tsp_exp2(m_run[rb] - m_new);
+        m_run[rb] = m_new;
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[rb][db][e] *= alpha;
+      }
+    };
+    // guard: a row may not have seen a visible key yet (m_run = -inf), so use 0 as its
+    // exponent offset; its scores are all -inf and its weights 0
+    auto softmax = [&](const tsp_f32x16(&sc)[RB], tsp_bf16x8(&pf)[RB][2], bool guard) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float mneg = (guard && m_run[rb] == -INFINITY) ? 0.f : -m_run[rb];
+        float lsum = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          float pw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pw[e] = tsp_exp2(fmaf(sc[rb][st * 8 + e], p.scale_log2, mneg));
+          tsp_u32x4 w;
+          w[0] = tsp_pack_bf16(pw[0], pw[1]);
+          w[1] = tsp_pack_bf16(pw[2], pw[3]);
+          w[2] = tsp_pack_bf16(pw[4], pw[5]);
+          w[3] = tsp_pack_bf16(pw[6], pw[7]);
+          // the row sum uses the rounded weights the PV product applies
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lsum = tsp_sum_bf16_pair(w[e], lsum);
+          pf[rb][st] = __builtin_bit_cast(tsp_bf16x8, w);
+        }
+        l_run[rb] += lsum;
+      }
+    };
+    auto pv = [&](int t, const tsp_bf16x8(&pf)[RB][2]) {
+      const uint8_t* vt =
+          smem + ((t / SPS) % NBUF) * St::SLOT_STRIDE + (t % SPS) * BK * St::ROW_BYTES;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const uint8_t* a = vt + voff[db] + st * 16 * St::ROW_BYTES;
+          const tsp_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a));
+          const tsp_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a + 8 * St::ROW_BYTES));
+          const tsp_bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb][st], acc[rb][db], 0, 0, 0);
+        }
+      }
+    };
+
+    // ---- prologue -------------------------------------------------------------------
+    __syncthreads();  // the previous tile's readers are done with every buffer
+    const int pro = min(PD, n_stage - 1);
+    for (int s = 0; s <= pro; ++s) issue_stage(s);
+    stage_ready(0, pro);
+
+    tsp_f32x16 s_cur[RB];
+    float mx[RB];
+    qk(0, s_cur);
+    if (needs_mask(0)) mask(0, s_cur);
+    rowmax(s_cur, mx);
+
+    // ---- main sweep ----------------------------------------------------------------------
+    // Fast path: steps whose successor needs no mask and whose prefetched stage lies fully
+    // below the end of its range. Unrolled over whole ring cycles so every LDS slot is a compile-time
+    // offset and the two score tiles alternate without copies; constant vmcnt; no clamping.
+    constexpr int VM_STEADY = St::LPW * (PD - 1);
+    static_assert(VM_STEADY < 16, "vmcnt immediate");
+    constexpr int GROUP = (NBUF * SPS) % 2 == 0 ? NBUF * SPS : 2 * NBUF * SPS;  // steps per unrolled group
+    int32_t n_full = kv_end / St::BKS;  // stages with every key below the end of their range
+    int32_t t_unmasked = t_mask;        // the steps from u_left up to it need no mask
+    if constexpr (NR == 2) {
+      if (run_on) {
+        n_full = n_stage1 + kv_end2 / St::BKS;
+        t_unmasked = T1 + t_mask2;
+      }
+    }
+    const int t_fast = u_left == 0 ? min(t_unmasked - 1, (n_full - PD) * SPS - 1) : 0;
+    tsp_f32x16 s_alt[RB];
+    // Stage boundary: wait until stage NEXT (relative to t0 / SPS) landed for every wave,
+    // then issue the stage PD ahead into the slot two stages back.
+    auto boundary = [&](auto next_const, int t0) {
+      constexpr int NEXT = decltype(next_const)::value;
+      __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // that stage landed (this wave's part)
+      __syncthreads();  // ... for every wave; the slot two stages back is free again
+      const int32_t sg = t0 / SPS + NEXT + PD;  // the stage to issue
+      int64_t adv = (int64_t)sg * stage_stride;
+      const uint16_t* kb = kbase;
+      const uint16_t* vb = vbase;
+      if constexpr (NR == 2) {
+        if (sg >= n_stage1) {  // a stage of the second range
+          kb = kbase2;
+          vb = vbase2;
+          adv -= stage_off2;
+        }
+      }
+      const uint32_t base = smem_addr + ((NEXT + PD) % NBUF) * St::SLOT_STRIDE;
+#pragma unroll
+      for (int q = 0; q < St::LPW; ++q)
+        tsp_lds_dma16((dma_isv[q] ? vb : kb) + adv, dma_voff[q], base + dma_slot[q]);
+    };
+    // LAG (second half of the waves, one of the two waves of each SIMD): the barrier of
+    // stage k comes after the PV products of step SPS*k - 2 instead of before the QK
+    // products of step SPS*k - 1. Every barrier still precedes the first read of its stage
+    // and follows the last read of the stage two back, but the two waves of a SIMD then run
+    // their matrix and vector phases in alternation (one's softmax under the other's MFMAs).
+    auto fast_step = [&](auto u_const, auto lag_const, int t0) {
+      constexpr int U = decltype(u_const)::value;  // step t = t0 + U, t0 a multiple of GROUP
+      constexpr bool LAG = decltype(lag_const)::value;
+      tsp_f32x16(&sc)[RB] = (U % 2 == 0) ? s_cur : s_alt;
+      tsp_f32x16(&sn)[RB] = (U % 2 == 0) ? s_alt : s_cur;
+      if (rescale_needed(mx)) rescale(mx);
+      if constexpr (!LAG && (U + 1) % SPS == 0)  // step t+1 opens a new stage
+        boundary(std::integral_constant<int, (U + 1) / SPS>{}, t0);
+      tsp_bf16x8 pf[RB][2];
+      qk(U + 1, sn);     // matrix pipe: next step's scores
+      softmax(sc, pf, false);  // vector pipe: this step's weights
+      pv(U, pf);         // matrix pipe: this step's output
+      if constexpr (LAG && (U + 2) % SPS == 0)  // the next stage's barrier, one phase early
+        boundary(std::integral_constant<int, (U + 2) / SPS>{}, t0);
+      rowmax(sn, mx);    // vector pipe: next step's row max
+    };
+    auto fast_group = [&]<int... Us>(std::integer_sequence<int, Us...>, auto lag_const, int t0) {
+      (fast_step(std::integral_constant<int, Us>{}, lag_const, t0), ...);
+    };
+    int t = 0;
+    constexpr bool PINGPONG = TSP_PINGPONG && SPS == 2 && NW % 2 == 0;
+    if (PINGPONG && TSP_PP_LAGGED(wave)) {
+      for (; t + GROUP <= t_fast; t += GROUP)
+        fast_group(std::make_integer_sequence<int, GROUP>{}, std::bool_constant<PINGPONG>{}, t);
+    } else {
+      for (; t + GROUP <= t_fast; t += GROUP)
+        fast_group(std::make_integer_sequence<int, GROUP>{}, std::false_type{}, t);
+    }
+    int issued = t > 0 ? t / SPS + PD : pro;  // last stage issued so far
+
+    // General path: the masked steps near the diagonal, the partial last stage and the
+    // ring drain.
+    for (; t < n_kv; ++t) {
+      if (rescale_needed(mx)) rescale(mx);
+      tsp_bf16x8 pf[RB][2];
+      if (t + 1 < n_kv) {
+        if ((t + 1) % SPS == 0) {
+          stage_ready((t + 1) / SPS, issued);
+          if (issued + 1 < n_stage) issue_stage(++issued);
+        }
+        qk(t + 1, s_alt);
+        softmax(s_cur, pf, true);
+        pv(t, pf);
+        if (needs_mask(t + 1)) mask(t + 1, s_alt);
+        rowmax(s_alt, mx);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_alt[rb];
+      } else {
+        softmax(s_cur, pf, true);
+        pv(t, pf);
+      }
     }
 
     // ---- epilogue: normalise, round to bf16, write O and lse -----------------------------

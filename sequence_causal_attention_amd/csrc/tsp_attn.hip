@@ -199,9 +199,24 @@ int tsp_attn_fwd_range2(const void* q_local, const void* k_full, const void* v_f
     return fail(TSP_EINVAL, "second key range [%lld, %lld) must lie inside [%lld, %lld]", (long long)kv_begin2,
                 (long long)kv_end2, (long long)kv_end, (long long)S_total);
   if (accumulate != 0 && accumulate != 1) return fail(TSP_EINVAL, "accumulate must be 0 or 1");
-  const bool two = kv_end2 > kv_begin2;
-  p.kv_lo = (int32_t)kv_begin;
-  p.kv_hi = (int32_t)kv_end;
+  // Keys past the rank's last query position (the end of its second chunk) are visible to
+  // no row: clip both ranges there, then let one range stand for two where the other is
+  // empty or they touch. The visible keys are the same; a single range runs the one-range
+  // kernel and, for fp32, one launch.
+  const int64_t seen = (2 * D - rank) * (S_total / (2 * D));  // keys [0, seen) are visible to some row
+  int64_t lo1 = kv_begin, hi1 = std::max(kv_begin, std::min(kv_end, seen));
+  int64_t lo2 = kv_begin2, hi2 = std::max(kv_begin2, std::min(kv_end2, seen));
+  if (hi1 == lo1) {  // the first range is empty: the second alone (or nothing)
+    lo1 = lo2;
+    hi1 = hi2;
+    lo2 = hi2 = S_total;
+  } else if (hi2 > lo2 && lo2 == hi1) {  // adjacent ranges: one range
+    hi1 = hi2;
+    lo2 = hi2 = S_total;
+  }
+  const bool two = hi2 > lo2;
+  p.kv_lo = (int32_t)lo1;
+  p.kv_hi = (int32_t)hi1;
   p.accumulate = accumulate;
   p.q = q_local;
   p.k = k_full;
@@ -212,8 +227,8 @@ int tsp_attn_fwd_range2(const void* q_local, const void* k_full, const void* v_f
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
   if (dtype == TSP_BF16) {
     if (two) {  // one sweep over both ranges
-      p.kv_lo2 = (int32_t)kv_begin2;
-      p.kv_hi2 = (int32_t)kv_end2;
+      p.kv_lo2 = (int32_t)lo2;
+      p.kv_hi2 = (int32_t)hi2;
     }
     switch (dh) {
       case 64: launch_bf16<64>(p, s); break;
@@ -224,8 +239,8 @@ int tsp_attn_fwd_range2(const void* q_local, const void* k_full, const void* v_f
     // fp32: one launch per range, the second merged into the first's result
     for (int rg = 0; rg < (two ? 2 : 1); ++rg) {
       if (rg == 1) {
-        p.kv_lo = (int32_t)kv_begin2;
-        p.kv_hi = (int32_t)kv_end2;
+        p.kv_lo = (int32_t)lo2;
+        p.kv_hi = (int32_t)hi2;
         p.accumulate = 1;
       }
       switch (dh) {

@@ -303,6 +303,11 @@ RANGE2_CASES = [  # (B, S_total, D, rank, Hq, Hkv, dh, dtype, first range, secon
     (1, 1200, 3, 2, 6, 2, 128, torch.bfloat16, (0, 200), (1000, 1200)),     # ragged chunks
     (2, 1024, 4, 1, 4, 2, 128, torch.bfloat16, (128, 256), (768, 896)),     # batch of 2
     (1, 4096, 1, 0, 4, 4, 128, torch.bfloat16, (17, 1000), (2000, 3001)),   # D = 1
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, (100, 650), (700, 1650)),   # unaligned, with a gap
+    (1, 2048, 8, 3, 4, 4, 128, torch.bfloat16, (0, 640), (704, 1664)),     # unmasked run into the second
+    (1, 2048, 8, 5, 4, 4, 128, torch.bfloat16, (320, 384), (1280, 1408)),  # peer 2's chunks
+    (1, 1024, 2, 1, 8, 2, 64, torch.bfloat16, (64, 300), (400, 700)),      # dh 64, unaligned
+    (1, 4096, 4, 2, 12, 2, 256, torch.bfloat16, (77, 1500), (2100, 3333)),  # dh 256, unaligned
     (1, 512, 4, 1, 4, 1, 64, torch.float32, (0, 64), (448, 512)),           # fp32
     (1, 600, 3, 1, 2, 1, 128, torch.float32, (37, 100), (451, 600)),        # fp32 ragged
 ]
@@ -427,3 +432,32 @@ def test_two_ranges_invalid_write_nothing():
         assert ei.value.status == tsp.TSP_EINVAL
     torch.cuda.synchronize()
     assert (out == 5).all() and (lse == 5).all()
+
+
+FOLD_CASES = [  # (rank, first, second, the one range it equals); S_total 2048, D 8, C 128
+    (3, (0, 128), (1920, 2048), (0, 128)),        # second past every position (peer 0 of rank 3)
+    (3, (896, 1024), (1024, 1152), (896, 1152)),  # adjacent chunks 7 and 8 (peer 7 of rank 3)
+    (3, (1700, 1800), (1800, 1900), (2048, 2048)),  # both past every position: nothing visible
+    (0, (0, 0), (100, 300), (100, 300)),          # empty first range
+]
+
+
+@pytest.mark.parametrize("accumulate", [False, True], ids=["write", "accumulate"])
+@pytest.mark.parametrize("case", FOLD_CASES, ids=lambda c: f"r{c[0]}_{c[1]}_{c[2]}")
+def test_two_ranges_that_fold_to_one_are_bitwise_one_range(case, accumulate):
+    """Ranges clipped at the rank's last position, an empty first range and adjacent ranges
+    run as one range: the result is the one-range call's, bit for bit."""
+    r, ra, rb, one = case
+    _note(f"fold {case} accumulate={accumulate}")
+    q, k, v = workloads.make_custom(1, 2048, 8, 4, 2, 128, torch.bfloat16, seed=47)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    res = []
+    for kw in (dict(kv_range=ra, kv_range2=rb), dict(kv_range=one)):
+        if accumulate:
+            o, l = tsp.fwd(qd, kd, vd, D=8, rank=r, kv_range=(1200, 1300))
+            tsp.fwd(qd, kd, vd, D=8, rank=r, out=o, lse=l, accumulate=True, **kw)
+        else:
+            o, l = tsp.fwd(qd, kd, vd, D=8, rank=r, **kw)
+        res.append((o, l))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
