@@ -303,6 +303,10 @@ def main():
     ap.add_argument("--balance", default=None, metavar="RANKS",
                     help="time the forward of several ranks of the workload instead (comma list, or "
                          "'all'); reports each rank's time and the max / min ratio")
+    ap.add_argument("--inputs", default="normal", choices=["normal", "zero-q", "zeros"],
+                    help="diagnostic: run the same launches on zero queries (zero-q) or on all-zero "
+                         "inputs (zeros) to show how the speed depends on the operand values; the "
+                         "line is then not the metric's workload (its data field says so)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run plain device copies of MIB MiB (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -342,6 +346,11 @@ def main():
 
     q, k, v = workloads.make_inputs(w, rank)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    if args.inputs != "normal":  # diagnostic only: same launches, other operand values
+        qd.zero_()
+        if args.inputs == "zeros":
+            kd.zero_()
+            vd.zero_()
     out = torch.empty_like(qd)
     lse = torch.empty((w.B, w.Hq, w.S_local), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream(dev)  # default priority
@@ -409,7 +418,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
 
     cpu = None
-    if not args.no_cpu_baseline and not args.chunk_pipeline and not args.backward:
+    if not args.no_cpu_baseline and not args.chunk_pipeline and not args.backward and args.inputs == "normal":
         cpu = cpu_baseline(w, rank, q, k, v, args.cpu_budget)
 
     line = {
@@ -425,7 +434,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic",
+        "data": "synthetic" if args.inputs == "normal" else
+                f"diagnostic: {args.inputs} inputs instead of N(0,1), not the metric's workload",
         "config": {
             "workload": w.name, "B": w.B, "S_total": w.S_total, "D": w.D, "rank": rank, "Hq": w.Hq,
             "Hkv": w.Hkv, "dh": w.dh, "local_queries": w.S_local, "flops_per_step": flops,
