@@ -279,7 +279,7 @@ def main():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--chunk-pipeline", nargs="?", const="fused", choices=["fused", "merge", "pairs"],
+    ap.add_argument("--chunk-pipeline", nargs="?", const="fused", choices=["fused", "merge", "pairs", "ring"],
                     default=None,
                     help="time the chunk-pipelined form instead: one key-range launch per gathered "
                          "chunk (2D of them, in ring arrival order), folded into the running result "
@@ -362,6 +362,10 @@ def main():
              for p in ((rank - s) % w.D for s in range(w.D))]
     bounds = [rng for pair in pairs for rng in pair]
     part_o, part_l = torch.empty_like(out), torch.empty_like(lse)
+    # ring form: every chunk's arrival flag already set (the gathered K/V is resident), so the
+    # kernel's waits pass at the first poll
+    ring_ready = torch.ones(2 * w.D, dtype=torch.int32, device=dev)
+    ring_status = torch.zeros(1, dtype=torch.int32, device=dev)
 
     if args.backward:
         tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream)
@@ -376,6 +380,10 @@ def main():
             return
         if not args.chunk_pipeline:
             tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream)
+            return
+        if args.chunk_pipeline == "ring":
+            tsp.fwd_ring(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, chunk_ready=ring_ready, ready_value=1,
+                         spin_limit=1 << 20, wait_status=ring_status, stream=stream)
             return
         if args.chunk_pipeline == "pairs":
             tsp.fwd(qd, kd, vd, D=w.D, rank=rank, out=out, lse=lse, stream=stream, kv_range=pairs[0][0],
@@ -409,6 +417,8 @@ def main():
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
     launch = step_stats(torch, stream, step)
+    if args.chunk_pipeline == "ring" and int(ring_status.item()) != 0:
+        raise RuntimeError("a ring wait gave up although every chunk was flagged present")
 
     # causal FLOPs: 2 products (forward) or 5 (backward) of 2*dh per visible pair per query head
     flops = (10.0 if args.backward else 4.0) * w.B * w.Hq * w.dh * w.C * (w.S_total + 1)
@@ -446,6 +456,8 @@ def main():
                      if args.chunk_pipeline == "fused" else
                      f"chunk pipeline: {len(pairs)} two-range launches (a peer's two chunks each), merged "
                      "in the epilogue" if args.chunk_pipeline == "pairs" else
+                     "chunk pipeline, ring order: the own chunks in one launch, every peer's chunks in a second "
+                     "(arrival flags polled per chunk), merged in its epilogue" if args.chunk_pipeline == "ring" else
                      f"chunk pipeline: {len(bounds)} key-range launches + {len(bounds) - 1} merge launches"),
         },
         "roofline": {

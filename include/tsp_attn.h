@@ -117,6 +117,37 @@ int tsp_attn_fwd_range2(const void* q_local, const void* k_full, const void* v_f
                         int64_t kv_begin2, int64_t kv_end2, int accumulate, int dtype, void* stream);
 
 /*
+ * tsp_attn_fwd_ring -- tsp_attn_fwd computed chunk by chunk in the order a ring all-gather
+ * of the zigzag chunks delivers them ("Folding Tensor and Sequence Parallelism ...",
+ * section 2 Methodology: K/V gathered along the sequence, zigzag partitioning), so that the
+ * attention can start before the gather has finished.
+ *
+ * Two launches on `stream`: the rank's own chunks r and 2D-1-r (as tsp_attn_fwd_range2,
+ * written fresh), then one sweep over the peers' chunks in arrival order -- for ring steps
+ * s = 1 .. D-1, chunks p and 2D-1-p of peer p = (rank - s) mod D -- each taken whole by
+ * the query rows that see it and merged into the first launch's result in the epilogue.
+ * Before reading chunk c (its keys [c*C, (c+1)*C) of k_full / v_full), the second launch
+ * waits until chunk_ready[c] == ready_value (device int32 [2D], read with system-scope
+ * acquire loads, so a writer on another stream, device or a DMA engine may set it while
+ * the kernel runs). With chunk_ready = NULL every chunk is taken as present. A wait polls
+ * at most spin_limit times; a wait that gives up sets bit 0 of *wait_status (device int32)
+ * and the sweep goes on with whatever the chunk holds, so the kernel always completes and
+ * the caller must treat out / lse as invalid whenever that bit is set (the caller clears
+ * *wait_status beforehand). The result equals tsp_attn_fwd's up to the rounding order of
+ * the sums.
+ *
+ * Arguments, layouts, ownership and the other errors as tsp_attn_fwd. bf16 only
+ * (TSP_EUNSUPPORTED for fp32). TSP_EUNSUPPORTED also when C is not a multiple of 64 or of
+ * the kernel's query tile (tsp_attn_schedule's rows per tile, 256 at dh 128), since every
+ * tile must lie in one chunk. TSP_EINVAL when chunk_ready is given without wait_status or
+ * with spin_limit < 1. With D = 1 only the first launch runs.
+ */
+int tsp_attn_fwd_ring(const void* q_local, const void* k_full, const void* v_full, void* out,
+                      float* lse, int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq,
+                      int64_t Hkv, int64_t dh, const int32_t* chunk_ready, int32_t ready_value,
+                      int32_t spin_limit, int32_t* wait_status, int dtype, void* stream);
+
+/*
  * tsp_attn_merge -- combine two partial results over disjoint key sets:
  *   lse = log(exp(lse_a) + exp(lse_b)),
  *   out = exp(lse_a - lse) * out_a + exp(lse_b - lse) * out_b,

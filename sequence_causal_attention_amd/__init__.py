@@ -41,6 +41,8 @@ SIGNATURES = {
                                           _I64, _I64, ctypes.c_int, ctypes.c_int, _VP]),
     "tsp_attn_fwd_range2": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                            _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int, _VP]),
+    "tsp_attn_fwd_ring": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                         _VP, ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int, _VP]),
     "tsp_attn_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "tsp_attn_bwd": (ctypes.c_int, [_VP] * 10 + [_I64] * 7 + [ctypes.c_int, _VP]),
     "tsp_gemm_bf16_nt": (ctypes.c_int, [_VP, _VP, _VP] + [_I64] * 6 + [ctypes.c_int, _VP]),
@@ -165,6 +167,54 @@ def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D:
             st = lib().tsp_attn_fwd_range2(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
                                            lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, lo, hi, lo2, hi2,
                                            int(bool(accumulate)), code, handle)
+    _check(st)
+    return out, lse
+
+
+def fwd_ring(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D: int, rank: int,
+             out: torch.Tensor | None = None, lse: torch.Tensor | None = None, chunk_ready: torch.Tensor | None = None,
+             ready_value: int = 1, spin_limit: int = 1 << 20, wait_status: torch.Tensor | None = None, stream=None):
+    """The same attention as fwd(), swept chunk by chunk in ring arrival order
+    (tsp_attn_fwd_ring): the rank's own two chunks in one launch, then every peer's chunks
+    in a second, which reads chunk c only once chunk_ready[c] == ready_value.
+
+    chunk_ready: int32 [2D] on the inputs' device, or None (all chunks present). With
+    flags, wait_status (int32 [1], same device) receives bit 0 if a wait gave up after
+    spin_limit polls. bf16 only. Returns (out, lse)."""
+    for name, t in (("q_local", q_local), ("k_full", k_full), ("v_full", v_full)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise TspAttnError(TSP_EINVAL, f"{name} must be a contiguous 4-D GPU tensor")
+    if not (q_local.dtype == k_full.dtype == v_full.dtype) or not (q_local.device == k_full.device == v_full.device):
+        raise TspAttnError(TSP_EINVAL, "q_local, k_full and v_full must share one dtype and device")
+    B, S_local, Hq, dh = q_local.shape
+    Bk, S_total, Hkv, dhk = k_full.shape
+    if tuple(v_full.shape) != tuple(k_full.shape) or Bk != B or dhk != dh:
+        raise TspAttnError(TSP_EINVAL, "k_full / v_full must be [B, S_total, Hkv, dh] matching q_local")
+    if D < 1 or S_total % (2 * D) != 0 or S_local != S_total // D:
+        raise TspAttnError(TSP_EINVAL, f"q_local must hold S_total / D = {S_total // max(D, 1)} rows")
+    code = _dtype_code(q_local)
+    out = torch.empty_like(q_local) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, Hq, S_local), dtype=torch.float32, device=q_local.device)
+    if out.shape != q_local.shape or out.dtype != q_local.dtype or not out.is_contiguous():
+        raise TspAttnError(TSP_EINVAL, "out must match q_local")
+    if tuple(lse.shape) != (B, Hq, S_local) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TspAttnError(TSP_EINVAL, "lse must be float32 [B, Hq, S_local]")
+    _on_device(q_local.device, out=out, lse=lse)
+    ready_ptr = status_ptr = None
+    if chunk_ready is not None:
+        if (chunk_ready.dtype != torch.int32 or chunk_ready.numel() != 2 * D or not chunk_ready.is_contiguous()
+                or wait_status is None or wait_status.dtype != torch.int32 or wait_status.numel() < 1):
+            raise TspAttnError(TSP_EINVAL, "chunk_ready must be int32 [2D] and wait_status int32 [1]")
+        _on_device(q_local.device, chunk_ready=chunk_ready, wait_status=wait_status)
+        ready_ptr, status_ptr = chunk_ready.data_ptr(), wait_status.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q_local.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q_local.device):
+        st = lib().tsp_attn_fwd_ring(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, ready_ptr, int(ready_value),
+                                     int(spin_limit), status_ptr, code, handle)
     _check(st)
     return out, lse
 

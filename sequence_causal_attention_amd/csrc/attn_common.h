@@ -37,6 +37,13 @@ struct TspParams {
   int32_t accumulate;    // 0: write (out, lse); 1: merge into the (out, lse) already there
   int64_t kv_stride;     // elements between consecutive keys of k / v (Hkv * dh when dense)
   float scale_log2;      // log2(e) / sqrt(dh): scores go straight to the exp2 domain
+  // ring sweep (the peers' chunks in arrival order): chunk c may be read once
+  // ready[c] == ready_value (ready NULL: every chunk is present); a wait gives up after
+  // spin_limit polls and then sets bit 0 of *wait_status
+  const int32_t* ready;
+  int32_t ready_value;
+  int32_t spin_limit;
+  int32_t* wait_status;
 };
 
 

@@ -43,6 +43,9 @@
 #ifndef TSP_PINGPONG
 #define TSP_PINGPONG 1
 #endif
+#ifndef TSP_RING_SCOPE
+#define TSP_RING_SCOPE __HIP_MEMORY_SCOPE_SYSTEM
+#endif
 #ifndef TSP_PP_LAGGED
 #define TSP_PP_LAGGED(w) ((w) >= NW / 2)
 #endif
@@ -139,6 +142,12 @@ struct Bf16Stage {
 // NR: key ranges of the launch, 1 ([kv_lo, kv_hi)) or 2 (also [kv_lo2, kv_hi2), after the
 // first): one sweep runs through both, the second range's stages following the first's in
 // the LDS ring, so the pipeline neither drains nor refills between them.
+// NR = 3 is the ring sweep over the peers' chunks: for ring steps s = 1 .. D-1 the chunks
+// p and 2D-1-p of peer p = (rank - s) mod D, in that order, each taken whole by a tile
+// whose rows lie in a later chunk and skipped otherwise (no chunk straddles a row's
+// position, so nothing is masked). The sweep runs over a virtual key axis (the visible
+// chunks back to back); each stage's physical keys come from the chunk cursor, which also
+// waits for the chunk's arrival flag before the first stage of a chunk is loaded.
 template <int DH, int NW, int RB, int NBUF, int SPS, int OCC, int NR>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p) {
   using St = Bf16Stage<DH, NW, NBUF, SPS>;
@@ -219,6 +228,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
   }
   const uint32_t smem_addr = __builtin_amdgcn_readfirstlane(tsp_lds_addr(smem));
   const float inv_scale_log2 = 1.0f / p.scale_log2;
+  uint64_t ring_seen = 0;  // ring sweep: chunks (below 64) whose arrival flag this wave has seen set
 
   for (int which = 0; which < 2; ++which) {
     const int32_t qt = which == 0 ? p.n_qtiles - 1 - pair : pair;
@@ -245,9 +255,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     const int32_t wave_min_pos = tsp_zigzag_position(min(wave_first, p.S_local - 1), p.C, p.D, p.rank);
 
     bool tile_sees = false;  // some key of the ranges is visible to some row of the tile
+    // ring sweep: the chunk holding the tile's rows, and the number of peer chunks it sees
+    const int32_t tile_chunk = row0 < p.C ? p.rank : 2 * p.D - 1 - p.rank;
+    int32_t ring_n = 0;
+    if constexpr (NR == 3) {
+      for (int32_t s = 1; s < p.D; ++s) {
+        const int32_t pp = (p.rank - s + p.D) % p.D;
+        ring_n += (pp < tile_chunk) + (2 * p.D - 1 - pp < tile_chunk);
+      }
+      tile_sees = ring_n > 0;
+    } else {
 #pragma unroll
-    for (int rg = 0; rg < NR; ++rg)
-      tile_sees |= min(rg == 0 ? p.kv_hi : p.kv_hi2, tile_end) > (rg == 0 ? p.kv_lo : p.kv_lo2);
+      for (int rg = 0; rg < NR; ++rg)
+        tile_sees |= min(rg == 0 ? p.kv_hi : p.kv_hi2, tile_end) > (rg == 0 ? p.kv_lo : p.kv_lo2);
+    }
     if (!tile_sees) {
       if (p.accumulate) continue;  // an empty partial leaves the running result as it is
 #pragma unroll
@@ -291,10 +312,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     // ---- the keys of the sweep --------------------------------------------------------
     // The sweep starts at the stage boundary at or below kv_lo; key indices below are
     // relative to it (keys in [kv_base, kv_lo) are loaded but masked).
-    const int32_t kv_base = (p.kv_lo / St::BKS) * St::BKS;
-    const int32_t kv_lo_rel = p.kv_lo - kv_base;
-    // relative end of the keys this tile sweeps: its last position, or the range end
-    const int32_t kv_end = min(p.kv_hi, tile_end) - kv_base;
+    const int32_t kv_base = NR == 3 ? 0 : (p.kv_lo / St::BKS) * St::BKS;
+    const int32_t kv_lo_rel = NR == 3 ? 0 : p.kv_lo - kv_base;
+    // relative end of the keys this tile sweeps: its last position, or the range end (the
+    // ring sweep: its visible chunks back to back)
+    const int32_t kv_end = NR == 3 ? ring_n * p.C : min(p.kv_hi, tile_end) - kv_base;
     const uint16_t* __restrict__ kbase = kg + ((int64_t)b * p.S_total + kv_base) * p.kv_stride + (int64_t)hk * DH;
     const uint16_t* __restrict__ vbase = vg + ((int64_t)b * p.S_total + kv_base) * p.kv_stride + (int64_t)hk * DH;
     int32_t n_kv1 = (kv_end + BK - 1) / BK;             // pipeline steps
@@ -305,7 +327,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     for (int rb = 0; rb < RB; ++rb) qpos[rb] = min(pos[rb], p.kv_hi - 1);
     // steps [u_left, t_mask) are visible to every row of the wave; earlier steps hold keys
     // below kv_lo, later ones keys past some row's position or the range end: all masked
-    int32_t t_mask = min(n_kv1, max(0, min(wave_min_pos + 1, p.kv_hi) - kv_base) / BK);
+    // (the ring sweep has no masked step)
+    int32_t t_mask = NR == 3 ? n_kv1 : min(n_kv1, max(0, min(wave_min_pos + 1, p.kv_hi) - kv_base) / BK);
     const int32_t u_left = (kv_lo_rel + BK - 1) / BK;
     // The second range (two-range launches): its stages follow the first range's whole
     // stages in the ring and its steps start at step T1; its keys are indexed from its own
@@ -340,6 +363,66 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     const int32_t n_kv = T1 + n_kv2;              // pipeline steps of both ranges
     const int32_t n_stage = n_stage1 + n_stage2;  // stages of both ranges
 
+    // ---- ring sweep: physical first key of virtual stage sg ------------------------------
+    // Stages are asked for in order, each once; the cursor moves to the next visible chunk
+    // at a chunk's first stage. The chunk's arrival is checked beforehand by ring_poll_upto.
+    constexpr int32_t RING_E_MAX = 1 << 20;
+    auto ring_advance = [&](int32_t& e) -> int32_t {  // next visible chunk after ring index e
+      const int32_t n_e = min(2 * (p.D - 1), RING_E_MAX);
+      int32_t c = 0;
+      do {
+        ++e;
+        const int32_t pp = (p.rank - (1 + e / 2) + p.D) % p.D;
+        c = (e & 1) ? 2 * p.D - 1 - pp : pp;
+      } while (c >= tile_chunk && e < n_e);
+      return c >= tile_chunk ? 0 : c;  // 0 not reached: the count of visible chunks bounds the calls
+    };
+    int32_t ring_e = -1, ring_chunk = 0, ring_next = 0;  // load cursor: ring index, chunk, next chunk's first stage
+    auto ring_stage_key = [&](int32_t sg) -> int32_t {
+      const int32_t spc = p.C / St::BKS;  // stages per chunk
+      if (sg == ring_next) {
+        ring_chunk = ring_advance(ring_e);
+        ring_next += spc;
+      }
+      return ring_chunk * p.C + (sg - (ring_next - spc)) * St::BKS;
+    };
+    // Arrival: before any stage up to sg_max is loaded, wait (bounded) for the chunks those
+    // stages start. Wave 0 alone reads the flags (the acquire invalidates the caches, which
+    // is costly when every wave does it), then a workgroup barrier orders every wave's
+    // stage loads after that acquire. A flag load also drains wave 0's in-flight stage
+    // loads (the compiler waits for every vector load before using its value), so this runs
+    // outside the unrolled steps, reads both chunks of a ring step at once, and skips chunks
+    // already seen present (also for the pair's other tile). Every wave takes the barrier
+    // at the same points: the chunk cursor is the same in all of them.
+    int32_t poll_e = -1, poll_next = 0, poll_done = 0;
+    auto ring_poll_upto = [&](int32_t sg_max) {
+      if (p.ready == nullptr) return;
+      const int32_t spc = p.C / St::BKS;
+      bool polled = false;
+      while (poll_next <= sg_max && poll_done < ring_n) {
+        const int32_t c = ring_advance(poll_e);
+        poll_next += spc;
+        ++poll_done;
+        polled = true;
+        if (wave != 0 || (c < 64 && ((ring_seen >> c) & 1))) continue;
+        const int32_t pp = (p.rank - (1 + poll_e / 2) + p.D) % p.D;
+        const int32_t ca = pp, cb = 2 * p.D - 1 - pp;  // the ring step's two chunks
+        bool arrived = false;
+        for (int32_t it = 0; it < p.spin_limit && !arrived; ++it) {
+          const int32_t fa = __hip_atomic_load(p.ready + ca, __ATOMIC_ACQUIRE, TSP_RING_SCOPE);
+          const int32_t fb = __hip_atomic_load(p.ready + cb, __ATOMIC_ACQUIRE, TSP_RING_SCOPE);
+          const bool ra = __builtin_amdgcn_readfirstlane(fa) == p.ready_value;
+          const bool rb = __builtin_amdgcn_readfirstlane(fb) == p.ready_value;
+          if (ra && ca < 64) ring_seen |= uint64_t(1) << ca;
+          if (rb && cb < 64) ring_seen |= uint64_t(1) << cb;
+          arrived = c == ca ? ra : rb;
+          if (!arrived) __builtin_amdgcn_s_sleep(2);
+        }
+        if (!arrived && lane == 0) atomicOr(p.wait_status, 1);
+      }
+      if (polled) __syncthreads();
+    };
+
     // ---- stage loads: global -> LDS, this wave's share --------------------------------
     // Any stage: rows past the tile's last position (or its range's end) are clamped to it
     // (never read past it).
@@ -347,6 +430,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       const uint16_t* kb = kbase;
       const uint16_t* vb = vbase;
       int32_t kv0 = s * St::BKS, end = kv_end;
+      if constexpr (NR == 3) {  // a whole stage of a visible chunk
+        ring_poll_upto(s);
+        const int32_t k0 = ring_stage_key(s);
+        const uint32_t base = smem_addr + (s % NBUF) * St::SLOT_STRIDE;
+#pragma unroll
+        for (int q = 0; q < St::LPW; ++q)
+          tsp_lds_dma16((dma_isv[q] ? vb : kb) + (int64_t)k0 * kv_row_stride, dma_voff[q], base + dma_slot[q]);
+        return;
+      }
       if constexpr (NR == 2) {
         if (s >= n_stage1) {  // a stage of the second range
           kb = kbase2;
@@ -536,6 +628,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       __syncthreads();  // ... for every wave; the slot two stages back is free again
       const int32_t sg = t0 / SPS + NEXT + PD;  // the stage to issue
       int64_t adv = (int64_t)sg * stage_stride;
+      if constexpr (NR == 3) adv = (int64_t)ring_stage_key(sg) * kv_row_stride;
       const uint16_t* kb = kbase;
       const uint16_t* vb = vbase;
       if constexpr (NR == 2) {
@@ -577,11 +670,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
     int t = 0;
     constexpr bool PINGPONG = TSP_PINGPONG && SPS == 2 && NW % 2 == 0;
     if (PINGPONG && TSP_PP_LAGGED(wave)) {
-      for (; t + GROUP <= t_fast; t += GROUP)
+      for (; t + GROUP <= t_fast; t += GROUP) {
+        if constexpr (NR == 3) ring_poll_upto(t / SPS + PD + GROUP / SPS);  // the stages this group loads
         fast_group(std::make_integer_sequence<int, GROUP>{}, std::bool_constant<PINGPONG>{}, t);
+      }
     } else {
-      for (; t + GROUP <= t_fast; t += GROUP)
+      for (; t + GROUP <= t_fast; t += GROUP) {
+        if constexpr (NR == 3) ring_poll_upto(t / SPS + PD + GROUP / SPS);
         fast_group(std::make_integer_sequence<int, GROUP>{}, std::false_type{}, t);
+      }
     }
     int issued = t > 0 ? t / SPS + PD : pro;  // last stage issued so far
 

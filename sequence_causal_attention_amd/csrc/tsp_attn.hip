@@ -100,6 +100,14 @@ void launch_bf16(const TspParams& p, hipStream_t stream) {
                        dim3(C::NW * 64), 0, stream, p);
 }
 
+// the ring sweep over the peers' chunks (bf16)
+template <int DH>
+void launch_bf16_ring(const TspParams& p, hipStream_t stream) {
+  using C = Bf16Cfg<DH>;
+  hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::SPS, C::OCC, 3>), dim3(p.n_units),
+                     dim3(C::NW * 64), 0, stream, p);
+}
+
 template <int DH>
 void launch_f32(const TspParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((tsp::attn_fwd_f32_kernel<DH>), dim3(p.n_units), dim3(256), 0, stream, p);
@@ -260,6 +268,52 @@ int tsp_attn_fwd_range(const void* q_local, const void* k_full, const void* v_fu
                        int64_t kv_begin, int64_t kv_end, int accumulate, int dtype, void* stream) {
   return tsp_attn_fwd_range2(q_local, k_full, v_full, out, lse, B, S_total, D, rank, Hq, Hkv, dh, kv_begin, kv_end,
                              S_total, S_total, accumulate, dtype, stream);
+}
+
+int tsp_attn_fwd_ring(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse,
+                      int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh,
+                      const int32_t* chunk_ready, int32_t ready_value, int32_t spin_limit, int32_t* wait_status,
+                      int dtype, void* stream) {
+  if (!q_local || !k_full || !v_full || !out || !lse) return fail(TSP_EINVAL, "null pointer argument");
+  if (!aligned16(q_local) || !aligned16(k_full) || !aligned16(v_full) || !aligned16(out) || !aligned16(lse))
+    return fail(TSP_EINVAL, "pointers must be 16-byte aligned");
+  if (chunk_ready && (!wait_status || spin_limit < 1))
+    return fail(TSP_EINVAL, "with arrival flags, wait_status must be given and spin_limit must be >= 1");
+  TspParams p{};
+  KernelShape ks{};
+  int st = plan(B, S_total, D, rank, Hq, Hkv, dh, dtype, &p, &ks);
+  if (st != TSP_OK) return st;
+  if (dtype != TSP_BF16) return fail(TSP_EUNSUPPORTED, "the ring sweep has a bf16 kernel only");
+  // every query tile lies in one chunk, and every chunk is whole stages (64 keys)
+  if (p.C % p.BQ != 0 || p.C % 64 != 0)
+    return fail(TSP_EUNSUPPORTED, "the ring sweep needs the chunk length (%d) to be a multiple of the query tile (%d) "
+                "and of 64", p.C, p.BQ);
+  // the rank's own two chunks first: one two-range launch, written fresh
+  const int64_t C = S_total / (2 * D);
+  st = tsp_attn_fwd_range2(q_local, k_full, v_full, out, lse, B, S_total, D, rank, Hq, Hkv, dh, rank * C,
+                           (rank + 1) * C, (2 * D - 1 - rank) * C, (2 * D - rank) * C, 0, dtype, stream);
+  if (st != TSP_OK || D == 1) return st;
+  // then the peers' chunks in arrival order, merged into that result in the epilogue
+  p.q = q_local;
+  p.k = k_full;
+  p.v = v_full;
+  p.out = out;
+  p.lse = lse;
+  p.accumulate = 1;
+  p.ready = chunk_ready;
+  p.ready_value = ready_value;
+  p.spin_limit = spin_limit;
+  p.wait_status = wait_status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  switch (dh) {
+    case 64: launch_bf16_ring<64>(p, s); break;
+    case 128: launch_bf16_ring<128>(p, s); break;
+    case 256: launch_bf16_ring<256>(p, s); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TSP_ELAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return tsp_host::ok();
 }
 
 int tsp_attn_fwd(const void* q_local, const void* k_full, const void* v_full, void* out, float* lse, int64_t B,
