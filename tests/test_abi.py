@@ -154,6 +154,32 @@ def test_second_range_must_follow_the_first(lib, r1, r2):
     assert "second key range" in lib.tsp_attn_last_error().decode()
 
 
+def _ring(lib, ptrs=None, ready=None, status=None, spin=16, **kw):
+    a = dict(VALID, dtype=tsp.TSP_BF16, S_total=4096, D=4, Hq=4, Hkv=2, dh=128)
+    a.update(kw)
+    q, k, v, o, l = ptrs if ptrs is not None else (_fake(),) * 5
+    return lib.tsp_attn_fwd_ring(q, k, v, o, l, a["B"], a["S_total"], a["D"], a["rank"], a["Hq"], a["Hkv"], a["dh"],
+                                 ready, 1, spin, status, a["dtype"], None)
+
+
+def test_ring_validation(lib):
+    """Rejected before anything is enqueued (no GPU needed)."""
+    assert _ring(lib, dtype=tsp.TSP_F32) == tsp.TSP_EUNSUPPORTED          # bf16 only
+    assert "bf16" in lib.tsp_attn_last_error().decode()
+    assert _ring(lib, S_total=512) == tsp.TSP_EUNSUPPORTED                # C = 64: below the 128-row query tile (GQA 2:1)
+    assert "multiple" in lib.tsp_attn_last_error().decode()
+    assert _ring(lib, ready=_fake()) == tsp.TSP_EINVAL                    # flags without a status word
+    assert _ring(lib, ready=_fake(), status=_fake(), spin=0) == tsp.TSP_EINVAL  # no poll allowed
+    assert _ring(lib, rank=4) == tsp.TSP_EINVAL
+    assert _ring(lib, dh=96) == tsp.TSP_EUNSUPPORTED
+    for i in range(5):
+        ptrs = [_fake()] * 5
+        ptrs[i] = None
+        assert _ring(lib, ptrs=ptrs) == tsp.TSP_EINVAL
+        ptrs[i] = _fake(0x100008)
+        assert _ring(lib, ptrs=ptrs) == tsp.TSP_EINVAL
+
+
 def test_range_shares_fwd_validation(lib):
     f = _fake()
     assert lib.tsp_attn_fwd_range(f, f, f, f, None, 1, 512, 4, 1, 4, 1, 64, 0, 512, 0, tsp.TSP_F32, None) == \
