@@ -123,3 +123,47 @@ def test_ring_refusals():
     st = tsp.lib().tsp_attn_fwd_ring(q.data_ptr(), k.data_ptr(), k.data_ptr(), out.data_ptr(), lse.data_ptr(), 1,
                                      1024, 4, 1, 2, 2, 128, ready.data_ptr(), 1, 10, None, tsp.TSP_BF16, None)
     assert st == tsp.TSP_EINVAL  # flags without a status word
+
+
+def test_ring_reads_chunks_only_after_they_arrive():
+    """K/V chunks delivered by host-to-device copies on a second stream while the ring
+    launch runs: the peers' chunks start as NaN on the device and each chunk's flag is
+    copied in after its data, so a chunk read before its flag would put NaN into the
+    result. The launch is enqueued first and the copies only afterwards (a host pause in
+    between), so its waits see the flags arrive."""
+    import time
+
+    B, S, D, r, Hq, Hkv, dh = 1, 4096, 4, 3, 4, 2, 128
+    _note("ring with chunks copied in during the launch")
+    w, q, k, v = _inputs(B, S, D, r, Hq, Hkv, dh, 52)
+    C = w.C
+    k_host, v_host = k.pin_memory(), v.pin_memory()
+    kd = torch.full(k.shape, float("nan"), dtype=k.dtype, device=DEV)
+    vd = torch.full(v.shape, float("nan"), dtype=v.dtype, device=DEV)
+    for c in (r, 2 * D - 1 - r):  # the rank's own chunks are local
+        kd[:, c * C:(c + 1) * C].copy_(k[:, c * C:(c + 1) * C])
+        vd[:, c * C:(c + 1) * C].copy_(v[:, c * C:(c + 1) * C])
+    qd = q.to(DEV)
+    ready = torch.zeros(2 * D, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    one = torch.ones(1, dtype=torch.int32).pin_memory()
+    compute, comm = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(comm):  # the first pinned copy of a process sets up its path (~15 ms)
+        torch.empty(1, dtype=torch.int32, device=DEV).copy_(one, non_blocking=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(compute):
+        out, lse = tsp.fwd_ring(qd, kd, vd, D=D, rank=r, chunk_ready=ready, ready_value=1, spin_limit=1 << 17,
+                                wait_status=status, stream=compute)
+    time.sleep(0.005)
+    with torch.cuda.stream(comm):
+        for s in range(1, D):  # ring order: both chunks of peer (r - s) mod D per step
+            p = (r - s) % D
+            for c in (p, 2 * D - 1 - p):
+                kd[:, c * C:(c + 1) * C].copy_(k_host[:, c * C:(c + 1) * C], non_blocking=True)
+                vd[:, c * C:(c + 1) * C].copy_(v_host[:, c * C:(c + 1) * C], non_blocking=True)
+                ready[c:c + 1].copy_(one, non_blocking=True)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "a wait gave up before its chunk arrived"
+    ref_out, ref_lse = oracle.causal_attention(q, k, v, D, r)
+    check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_out, ref_lse,
+          torch.bfloat16, C=w.C)
