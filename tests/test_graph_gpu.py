@@ -124,3 +124,27 @@ def test_fwd_bwd_graph_replays(dh):
         for name, a, b in zip(("out", "lse", "dq", "dk", "dv", "delta"), (out, lse, dq, dk, dv, delta), ref):
             assert torch.equal(a, b), f"replay {i}: {name}"
         _eager_noise()
+
+
+def test_ring_graph_replays():
+    """tsp_attn_fwd_ring (two launches, arrival flags set) captured once and replayed."""
+    _note("graph ring")
+    S, D, r, Hq, Hkv, dh = 4096, 4, 2, 4, 2, 128
+    q, k, v = (t.to(DEV) for t in workloads.make_custom(1, S, D, Hq, Hkv, dh, torch.bfloat16, seed=68))
+    ready = torch.ones(2 * D, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ref_o, ref_l = tsp.fwd_ring(q, k, v, D=D, rank=r, chunk_ready=ready, ready_value=1, spin_limit=1 << 10,
+                                wait_status=status)
+    torch.cuda.synchronize()
+    out, lse = torch.empty_like(q), torch.empty_like(ref_l)
+    g = _capture(lambda: tsp.fwd_ring(q, k, v, D=D, rank=r, out=out, lse=lse, chunk_ready=ready, ready_value=1,
+                                      spin_limit=1 << 10, wait_status=status))
+    for i in range(3):
+        out.fill_(7.0)
+        lse.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
+        _eager_noise()
