@@ -167,3 +167,22 @@ def test_ring_reads_chunks_only_after_they_arrive():
     ref_out, ref_lse = oracle.causal_attention(q, k, v, D, r)
     check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_out, ref_lse,
           torch.bfloat16, C=w.C)
+
+
+def test_ring_gqa_shard_sampled_rows():
+    """The GQA dh-256 shard at full size (S_total 65536, D 4, rank 2, 24 query heads on 4
+    KV heads): 64-row query tiles, 32-key stages."""
+    w = workloads.BY_NAME["gqa_shard_s64k"]
+    r = 2
+    _note("ring GQA shard rank 2")
+    q, k, v = workloads.make_inputs(w, r)
+    ready = torch.ones(2 * w.D, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out, lse = tsp.fwd_ring(q.to(DEV), k.to(DEV), v.to(DEV), D=w.D, rank=r, chunk_ready=ready, ready_value=1,
+                            spin_limit=1 << 10, wait_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    rows = sample_rows(w, n_random=24)
+    ref_out, ref_lse = oracle.causal_attention(q, k, v, w.D, r, rows=rows, block=64)
+    check(out.float().cpu().numpy()[:, rows].astype(np.float64), lse.cpu().numpy()[:, :, rows].astype(np.float64),
+          ref_out, ref_lse, torch.bfloat16, C=w.C, rows=rows)
