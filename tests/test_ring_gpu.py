@@ -148,11 +148,12 @@ def test_ring_reads_chunks_only_after_they_arrive():
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     one = torch.ones(1, dtype=torch.int32).pin_memory()
     compute, comm = torch.cuda.Stream(), torch.cuda.Stream()
-    with torch.cuda.stream(comm):  # the first pinned copy of a process sets up its path (~15 ms)
+    with torch.cuda.stream(comm):  # the first pinned copies of a process set up their path (~15 ms)
         torch.empty(1, dtype=torch.int32, device=DEV).copy_(one, non_blocking=True)
+        torch.empty_like(kd[:, :C]).copy_(k_host[:, :C], non_blocking=True)
     torch.cuda.synchronize()
     with torch.cuda.stream(compute):
-        out, lse = tsp.fwd_ring(qd, kd, vd, D=D, rank=r, chunk_ready=ready, ready_value=1, spin_limit=1 << 17,
+        out, lse = tsp.fwd_ring(qd, kd, vd, D=D, rank=r, chunk_ready=ready, ready_value=1, spin_limit=1 << 19,
                                 wait_status=status, stream=compute)
     time.sleep(0.005)
     with torch.cuda.stream(comm):
