@@ -30,18 +30,22 @@ METRIC = "causal attention TFLOP/s per rank shard + % of bf16 MFMA peak (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-# the sources of the forward kernel and of its launch configuration, and the build script
-# that holds its compile flags
+# the sources of the forward kernel and of its launch configuration; its compile flags are
+# taken from the build script's entry for that unit
 FORWARD_SOURCES = ("csrc/attn_common.h", "csrc/attn_fwd_bf16.h", "csrc/attn_fwd_f32.h", "csrc/zigzag.h",
-                   "csrc/tsp_attn.hip", "build.py")
+                   "csrc/tsp_attn.hip")
 
 
 def kernel_source_digest() -> str:
+    from sequence_causal_attention_amd import build as b
+
     pkg = os.path.join(ROOT, "sequence_causal_attention_amd")
     h = hashlib.sha256()
     for name in FORWARD_SOURCES:
         with open(os.path.join(pkg, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
+    flags = [fl for src, fl in b.UNITS if os.path.basename(src) == "tsp_attn.hip"]
+    h.update(repr((b.COMMON, flags)).encode())
     return h.hexdigest()[:16]
 
 
