@@ -26,9 +26,11 @@ UNITS = [
     (os.path.join(CSRC, "tsp_attn.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans",
                                           "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]),
     # backward kernels, dh 64 / 128: MFMA results in arch VGPRs; LLVM's max-ilp scheduling
-    # strategy (+1.9-2.5% on the 7B shard backward in A/B runs, same results bit for bit)
+    # strategy (+1.9-2.5% on the 7B shard backward in A/B runs) with its own register
+    # pressure trackers (+1.1-1.8% more); same results bit for bit
     (os.path.join(CSRC, "tsp_attn_bwd.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
-                                              "-mllvm", "-amdgpu-sched-strategy=max-ilp"]),
+                                              "-mllvm", "-amdgpu-sched-strategy=max-ilp",
+                                              "-mllvm", "-amdgpu-use-amdgpu-trackers"]),
     # backward kernels, dh 256: the dK/dV accumulators fill the arch VGPRs, so MFMA
     # results stay in the accumulation registers; max-ilp scheduling (+9.5% on the GQA
     # dh-256 shard backward in an A/B run, same results bit for bit)
