@@ -32,8 +32,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 # the sources of the forward kernel and of its launch configuration; its compile flags are
 # taken from the build script's entry for that unit
-FORWARD_SOURCES = ("csrc/attn_common.h", "csrc/attn_fwd_bf16.h", "csrc/attn_fwd_f32.h", "csrc/zigzag.h",
-                   "csrc/tsp_attn.hip")
+FORWARD_SOURCES = ("csrc/attn_common.h", "csrc/attn_fwd_bf16.h", "csrc/zigzag.h", "csrc/host_common.h",
+                   "csrc/tsp_attn_fwd_bf16.hip", "csrc/tsp_attn.hip")
+FORWARD_UNIT = "tsp_attn_fwd_bf16.hip"
 
 
 def kernel_source_digest() -> str:
@@ -44,7 +45,7 @@ def kernel_source_digest() -> str:
     for name in FORWARD_SOURCES:
         with open(os.path.join(pkg, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
-    flags = [fl for src, fl in b.UNITS if os.path.basename(src) == "tsp_attn.hip"]
+    flags = [fl for src, fl in b.UNITS if os.path.basename(src) == FORWARD_UNIT]
     h.update(repr((b.COMMON, flags)).encode())
     return h.hexdigest()[:16]
 

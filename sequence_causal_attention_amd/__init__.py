@@ -21,7 +21,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtsp_attn.so")
+# TSP_ATTN_LIB names another build of the same library (the host-sanitized one of the
+# build script's --host-sanitize check); by default the in-tree libtsp_attn.so
+LIB_PATH = os.environ.get("TSP_ATTN_LIB") or os.path.join(_HERE, "libtsp_attn.so")
 
 TSP_OK = 0
 TSP_EINVAL = -1
@@ -117,6 +119,7 @@ def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D:
     q_local [B, 2C, Hq, dh], k_full / v_full [B, S_total, Hkv, dh]: contiguous, same
     device and dtype (bf16 or fp32). Returns (out [B, 2C, Hq, dh] same dtype,
     lse [B, Hq, 2C] fp32). ``out`` / ``lse`` may be passed in preallocated.
+    Without a key range this is ``tsp_attn_fwd``.
     ``kv_range=(begin, end)`` restricts the keys (tsp_attn_fwd_range): rows without a
     visible key in the range get out = 0, lse = -inf. With ``accumulate=True`` the
     partial over the range is merged into the ``out`` / ``lse`` passed in (a result over
@@ -158,7 +161,10 @@ def fwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, *, D:
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     lo, hi = (0, S_total) if kv_range is None else (int(kv_range[0]), int(kv_range[1]))
     with torch.cuda.device(q_local.device):
-        if kv_range2 is None:
+        if kv_range is None and kv_range2 is None and not accumulate:  # the whole key sequence
+            st = lib().tsp_attn_fwd(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, code, handle)
+        elif kv_range2 is None:
             st = lib().tsp_attn_fwd_range(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
                                           lse.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, lo, hi,
                                           int(bool(accumulate)), code, handle)
@@ -249,11 +255,9 @@ def merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor, lse_b: 
     return out, lse
 
 
-def bwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
-        dout: torch.Tensor, *, D: int, rank: int, dq=None, dk=None, dv=None, delta=None, stream=None):
-    """Backward of ``fwd`` (tsp_attn_bwd): returns (dq [B, 2C, Hq, dh], dk, dv
-    [B, S_total, Hkv, dh] -- this rank's partial K/V gradients -- and delta [B, Hq, 2C]).
-    Outputs may be passed in preallocated. bf16 or fp32."""
+def _bwd_check(q_local, k_full, v_full, out, lse, dout, outputs):
+    """Validates the backward's tensors; `outputs` are (name, tensor, like) triples.
+    Returns (B, S_local, Hq, dh, S_total, Hkv, dtype code)."""
     ins = (("q_local", q_local), ("k_full", k_full), ("v_full", v_full), ("out", out), ("dout", dout))
     for name, t in ins + (("lse", lse),):
         if not t.is_cuda or not t.is_contiguous():
@@ -269,18 +273,33 @@ def bwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, out: 
     if tuple(lse.shape) != (B, Hq, S_local) or lse.dtype != torch.float32:
         raise TspAttnError(TSP_EINVAL, "lse must be float32 [B, Hq, S_local]")
     code = _dtype_code(q_local)
+    for name, t, ref in outputs:
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise TspAttnError(TSP_EINVAL, f"{name} must match {tuple(ref.shape)} {ref.dtype}")
+    _on_device(q_local.device, k_full=k_full, v_full=v_full, out=out, lse=lse, dout=dout,
+               **{name: t for name, t, _ in outputs})
+    return B, S_local, Hq, dh, S_total, Hkv, code
+
+
+def _handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def bwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, *, D: int, rank: int, dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Backward of ``fwd`` (tsp_attn_bwd): returns (dq [B, 2C, Hq, dh], dk, dv
+    [B, S_total, Hkv, dh] -- this rank's partial K/V gradients -- and delta [B, Hq, 2C]).
+    Outputs may be passed in preallocated. bf16 or fp32."""
     dq = torch.empty_like(q_local) if dq is None else dq
     dk = torch.empty_like(k_full) if dk is None else dk
     dv = torch.empty_like(v_full) if dv is None else dv
     delta = torch.empty_like(lse) if delta is None else delta
-    for name, t, ref in (("dq", dq, q_local), ("dk", dk, k_full), ("dv", dv, v_full), ("delta", delta, lse)):
-        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise TspAttnError(TSP_EINVAL, f"{name} must match {tuple(ref.shape)} {ref.dtype}")
-    _on_device(q_local.device, k_full=k_full, v_full=v_full, out=out, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv,
-               delta=delta)
-    if stream is None:
-        stream = torch.cuda.current_stream(q_local.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    B, S_local, Hq, dh, S_total, Hkv, code = _bwd_check(
+        q_local, k_full, v_full, out, lse, dout,
+        (("dq", dq, q_local), ("dk", dk, k_full), ("dv", dv, v_full), ("delta", delta, lse)))
+    handle = _handle(stream, q_local.device)
     with torch.cuda.device(q_local.device):
         st = lib().tsp_attn_bwd(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
                                 lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),

@@ -106,4 +106,12 @@ int attn_plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, i
               TspParams* p);
 int attn_launch(const TspParams& p, int64_t dh, int dtype, hipStream_t stream);
 
+// The bf16 forward kernels (tsp_attn_fwd_bf16.hip): the query-tile shape per head dim, and
+// the launches of a planned forward (one key range, or two when kv_hi2 > kv_lo2) and of
+// the ring sweep over the peers' chunks. Each returns false for a head dim without a
+// kernel (nothing is launched then).
+bool bf16_kernel_shape(int64_t dh, KernelShape* ks);
+bool launch_fwd_bf16(const TspParams& p, int64_t dh, hipStream_t stream);
+bool launch_fwd_bf16_ring(const TspParams& p, int64_t dh, hipStream_t stream);
+
 }  // namespace tsp_host

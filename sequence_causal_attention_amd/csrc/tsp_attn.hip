@@ -1,13 +1,14 @@
 // tsp_attn.hip -- C ABI of the per-rank zigzag / GQA causal attention forward (gfx950):
-// argument validation, work decomposition, kernel dispatch, the zigzag map helpers and
-// the error strings. The operation and every argument are documented in tsp_attn.h.
+// argument validation, work decomposition, kernel dispatch, the fp32 forward, the merge,
+// the Ulysses layout changes, the zigzag map helpers and the error strings. The bf16
+// forward kernels live in tsp_attn_fwd_bf16.hip (their own code-generation flags). The
+// operation and every argument are documented in tsp_attn.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 
 #include "tsp_attn.h"
 #include "attn_common.h"
-#include "attn_fwd_bf16.h"
 #include "attn_fwd_f32.h"
 #include "attn_merge.h"
 #include "ulysses_permute.h"
@@ -24,54 +25,8 @@ using tsp_host::check_sizes;
 using tsp_host::fail;
 using tsp_host::KernelShape;
 
-// Tile configuration of the bf16 kernels per head dim: waves per workgroup, 32-row query
-// blocks per wave, depth of the LDS stage ring, target waves per SIMD.
-#ifndef TSP_DH128_NW
-#define TSP_DH128_NW 8
-#endif
-#ifndef TSP_DH128_NBUF
-#define TSP_DH128_NBUF 5
-#endif
-#ifndef TSP_DH128_SPS
-#define TSP_DH128_SPS 2
-#endif
-#ifndef TSP_DH128_RB
-#define TSP_DH128_RB 1
-#endif
-#ifndef TSP_DH128_OCC
-#define TSP_DH128_OCC 2
-#endif
-template <int DH>
-struct Bf16Cfg;
-template <>
-struct Bf16Cfg<64> {
-  static constexpr int NW = 4, RB = 2, NBUF = 4, SPS = 1, OCC = 1;
-};
-template <>
-struct Bf16Cfg<128> {
-  static constexpr int NW = TSP_DH128_NW, RB = TSP_DH128_RB, NBUF = TSP_DH128_NBUF, SPS = TSP_DH128_SPS,
-                       OCC = TSP_DH128_OCC;
-};
-template <>
-struct Bf16Cfg<256> {
-  static constexpr int NW = 4, RB = 1, NBUF = 4, SPS = 1, OCC = 1;
-};
-
-template <int DH>
-KernelShape bf16_shape() {
-  using C = Bf16Cfg<DH>;
-  return KernelShape{tsp::Bf16Stage<DH, C::NW, C::NBUF, C::SPS>::BK, C::NW, C::RB};
-}
-
 bool kernel_shape(int dtype, int64_t dh, KernelShape* ks) {
-  if (dtype == TSP_BF16) {
-    switch (dh) {
-      case 64: *ks = bf16_shape<64>(); return true;
-      case 128: *ks = bf16_shape<128>(); return true;
-      case 256: *ks = bf16_shape<256>(); return true;
-    }
-    return false;
-  }
+  if (dtype == TSP_BF16) return tsp_host::bf16_kernel_shape(dh, ks);
   if (dtype == TSP_F32 && (dh == 64 || dh == 128 || dh == 256)) {
     *ks = KernelShape{32, 4, 1};
     return true;
@@ -87,25 +42,6 @@ int plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_
   if (dtype != TSP_BF16 && dtype != TSP_F32) return fail(TSP_EUNSUPPORTED, "unknown dtype %d", dtype);
   if (!kernel_shape(dtype, dh, ks)) return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
   return tsp_host::plan_tiles(B, S_total, D, rank, Hq, Hkv, dh, *ks, p);
-}
-
-template <int DH>
-void launch_bf16(const TspParams& p, hipStream_t stream) {
-  using C = Bf16Cfg<DH>;
-  if (p.kv_hi2 > p.kv_lo2)  // two key ranges in one sweep
-    hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::SPS, C::OCC, 2>), dim3(p.n_units),
-                       dim3(C::NW * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::SPS, C::OCC, 1>), dim3(p.n_units),
-                       dim3(C::NW * 64), 0, stream, p);
-}
-
-// the ring sweep over the peers' chunks (bf16)
-template <int DH>
-void launch_bf16_ring(const TspParams& p, hipStream_t stream) {
-  using C = Bf16Cfg<DH>;
-  hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::SPS, C::OCC, 3>), dim3(p.n_units),
-                     dim3(C::NW * 64), 0, stream, p);
 }
 
 template <int DH>
@@ -166,12 +102,8 @@ int attn_plan(int64_t B, int64_t S_total, int64_t D, int64_t rank, int64_t Hq, i
 int attn_launch(const TspParams& p, int64_t dh, int dtype, hipStream_t stream) {
   (void)hipGetLastError();
   if (dtype == TSP_BF16) {
-    switch (dh) {
-      case 64: launch_bf16<64>(p, stream); break;
-      case 128: launch_bf16<128>(p, stream); break;
-      case 256: launch_bf16<256>(p, stream); break;
-      default: return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
-    }
+    if (!tsp_host::launch_fwd_bf16(p, dh, stream))
+      return fail(TSP_EUNSUPPORTED, "head dim %lld not in {64, 128, 256}", (long long)dh);
   } else {
     switch (dh) {
       case 64: launch_f32<64>(p, stream); break;
@@ -238,11 +170,7 @@ int tsp_attn_fwd_range2(const void* q_local, const void* k_full, const void* v_f
       p.kv_lo2 = (int32_t)lo2;
       p.kv_hi2 = (int32_t)hi2;
     }
-    switch (dh) {
-      case 64: launch_bf16<64>(p, s); break;
-      case 128: launch_bf16<128>(p, s); break;
-      case 256: launch_bf16<256>(p, s); break;
-    }
+    tsp_host::launch_fwd_bf16(p, dh, s);
   } else {
     // fp32: one launch per range, the second merged into the first's result
     for (int rg = 0; rg < (two ? 2 : 1); ++rg) {
@@ -306,11 +234,7 @@ int tsp_attn_fwd_ring(const void* q_local, const void* k_full, const void* v_ful
   p.wait_status = wait_status;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  switch (dh) {
-    case 64: launch_bf16_ring<64>(p, s); break;
-    case 128: launch_bf16_ring<128>(p, s); break;
-    case 256: launch_bf16_ring<256>(p, s); break;
-  }
+  tsp_host::launch_fwd_bf16_ring(p, dh, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TSP_ELAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return tsp_host::ok();

@@ -1,7 +1,7 @@
 """Pins for the fp64 oracle: checks against what the pages and the mathematics fix.
 
 Each ``pin_*`` takes an oracle namespace ``o`` (attributes ``causal_attention``,
-``causal_attention_bruteforce``, ``zigzag_positions``, ``unmasked_pairs``,
+``causal_attention_bruteforce``, ``zigzag_positions``, ``unmasked_pairs``, ``causal_flops``,
 ``kv_head_of``, ``causal_attention_range``, ``merge_partials``,
 ``causal_attention_backward``, ``ulysses``, ``tsp_layer``) and raises AssertionError when the
 implementation breaks the pin. The
@@ -65,6 +65,37 @@ def pin_pairs_closed_form(o):
         C = S // (2 * D)
         for r in range(D):
             assert int(o.unmasked_pairs(S, D, r)) == C * (S + 1), (S, D, r)
+
+
+def pin_causal_flops(o):
+    """The algorithmic FLOP count: per visible (query, key) pair and query head, one dot
+    product of length dh for the score (dh multiplies, dh adds) and one scaled row of V
+    added into the output (dh multiplies, dh adds).
+
+    Checked by counting those operations pair by pair with scalar loops on tiny shards
+    (positions built here from the chunk definition: chunk r, then chunk 2D-1-r), and
+    against the per-workload counts of the five measured shapes as printed to 4-5
+    significant digits (3.362e7, 1.0995e12, 1.3194e13, 1.7592e13, 1.0555e14).
+    """
+    for B, S, D, r, Hq, dh in [(1, 8, 1, 0, 1, 4), (2, 24, 3, 1, 3, 8), (1, 40, 4, 3, 2, 16), (3, 28, 7, 6, 5, 2)]:
+        C = S // (2 * D)
+        positions = list(range(r * C, (r + 1) * C)) + list(range((2 * D - 1 - r) * C, (2 * D - r) * C))
+        ops = 0
+        for _b in range(B):
+            for _h in range(Hq):
+                for p in positions:
+                    for j in range(S):
+                        if j <= p:
+                            ops += dh + dh  # score: multiplies and adds of the dot product
+                            ops += dh + dh  # output: weight times value row, added in
+        assert int(o.causal_flops(B, Hq, dh, S, D, r)) == ops, (B, S, D, r, Hq, dh)
+    printed = [((1, 4, 64, 512, 4, 1), 3.362e7), ((1, 32, 128, 32768, 8, 3), 1.0995e12),
+               ((1, 24, 256, 65536, 4, 2), 1.3194e13), ((1, 4, 128, 131072, 1, 0), 1.7592e13),
+               ((1, 24, 256, 262144, 8, 0), 1.0555e14), ((1, 24, 256, 262144, 8, 7), 1.0555e14)]
+    for args, want in printed:
+        got = float(o.causal_flops(*args))
+        digits = 10 ** (math.floor(math.log10(want)) - 3)  # the last printed digit
+        assert abs(got - want) <= digits, (args, got, want)
 
 
 def pin_gqa_ownership(o):
@@ -518,6 +549,7 @@ ALL_PINS = [
     pin_zigzag_golden,
     pin_zigzag_permutation,
     pin_pairs_closed_form,
+    pin_causal_flops,
     pin_gqa_ownership,
     pin_bruteforce,
     pin_sdpa_one_rank,

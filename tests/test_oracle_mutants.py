@@ -3,7 +3,8 @@
 Every mutant is a copy of the oracle with one plausible error: a swapped or mirrored
 chunk, a strict causal diagonal, interleaved GQA grouping, a wrong softmax scale, a
 base-2 lse, a dropped normalisation, swapped K/V operands, local instead of global
-positions, or a block-boundary error in the blocked form; and, for the backward, a dropped
+positions, a block-boundary error in the blocked form, or a FLOP count with one product
+per pair or without the causal mask; and, for the backward, a dropped
 softmax-Jacobian term, an unscaled dQ, a wrong operand or an overwritten GQA sum in dK,
 unnormalised weights in dV, or a strict diagonal.
 """
@@ -45,6 +46,10 @@ PATCHES = {
     "gqa_interleaved": ("kv_head_of", lambda h, Hq, Hkv: h % Hkv),
     "scale_one_over_dh": ("softmax_scale", lambda dh: 1.0 / dh),
     "no_scale": ("softmax_scale", lambda dh: 1.0),
+    # FLOP count with one product per pair instead of two
+    "flops_one_product": ("causal_flops", lambda B, Hq, dh, S, D, r: 2 * B * Hq * dh * A.unmasked_pairs(S, D, r)),
+    # FLOP count over the rank's local rows times all keys (no causal mask)
+    "flops_dense": ("causal_flops", lambda B, Hq, dh, S, D, r: 4 * B * Hq * dh * (S // D) * S),
 }
 
 
@@ -88,7 +93,7 @@ WRAPS = {
 def _namespace():
     ns = types.SimpleNamespace()
     for n in ("causal_attention", "causal_attention_bruteforce", "zigzag_positions",
-              "unmasked_pairs", "kv_head_of", "causal_attention_range", "merge_partials",
+              "unmasked_pairs", "causal_flops", "kv_head_of", "causal_attention_range", "merge_partials",
               "causal_attention_backward"):
         setattr(ns, n, getattr(A, n))
     ns.ulysses = U

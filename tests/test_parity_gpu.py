@@ -89,16 +89,45 @@ def test_small_shard_matches_oracle(case):
 
 # -- the workloads at their real sizes: sampled rows, all heads -------------------------
 
-def sample_rows(w, n_random=48, seed=0):
-    C = w.C
-    rows = {0, 1, 2, C - 2, C - 1, C, C + 1, 2 * C - 2, 2 * C - 1}
-    for t in (63, 64, 127, 128, 255, 256):
-        for base in (0, C):
+def sample_rows(w, n_random=512, seed=0, edge=64, tile_block=256):
+    """Local rows compared at full size: the first and last `edge` rows of each chunk,
+    rows on both sides of every 64-row boundary up to 256, `n_random` seeded random rows,
+    and a complete block of `tile_block` rows in the middle of the first chunk together
+    with its mirror image in the second chunk. The kernels process local rows in
+    mirrored pairs of query tiles (tile p with tile n-1-p) of 64, 128 or 256 rows, all of
+    which divide `tile_block`, so the block and its mirror hold every row of whole
+    workgroups."""
+    C, S = w.C, w.S_local
+    rows = set()
+    for base in (0, C):
+        rows.update(range(base, base + min(edge, C)))
+        rows.update(range(base + max(0, C - edge), base + C))
+        for t in (63, 64, 127, 128, 255, 256):
             if t < C:
                 rows.add(base + t)
+    if S >= 2 * tile_block and S % tile_block == 0:
+        a = (C // 2 // tile_block) * tile_block
+        rows.update(range(a, a + tile_block))
+        rows.update(range(S - a - tile_block, S - a))
     rng = np.random.default_rng(seed)
-    rows.update(int(x) for x in rng.integers(0, 2 * C, n_random))
-    return np.array(sorted(x for x in rows if 0 <= x < 2 * C))
+    rows.update(int(x) for x in rng.integers(0, S, n_random))
+    return np.array(sorted(x for x in rows if 0 <= x < S))
+
+
+def oracle_rows(q, k, v, D, r, rows, block=64):
+    """The oracle on the given rows, one query head per worker thread (numpy's kernels
+    run without the interpreter lock; the threaded BLAS is held to one thread each)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    Hq = q.shape[2]
+    n = max(1, min(16, os.cpu_count() or 1, Hq))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(n) as ex:
+        parts = list(ex.map(lambda h: oracle.causal_attention(q, k, v, D, r, rows=rows, heads=[h], block=block),
+                            range(Hq)))
+    return np.concatenate([o for o, _ in parts], axis=2), np.concatenate([l for _, l in parts], axis=1)
 
 
 def _rank_cases():
@@ -112,14 +141,41 @@ def _rank_cases():
 @pytest.mark.parametrize("wr", _rank_cases(), ids=lambda wr: f"{wr[0].name}_r{wr[1]}")
 def test_workload_sampled_rows_match_oracle(wr):
     w, r = wr
-    _note(f"workload {w.name} rank {r}")
     q, k, v = workloads.make_inputs(w, r)
+    # dh-256 tiles are 64 or 128 rows; 128 random rows at 256K keys keep the oracle near a minute
+    rows = np.arange(w.S_local) if w.index == 0 else sample_rows(
+        w, n_random=512 if w.S_total <= 131072 else 128, tile_block=256 if w.dh <= 128 else 128)
+    _note(f"workload {w.name} rank {r}: {len(rows)} rows, all {w.Hq} heads")
     out, lse = run(q, k, v, w.D, r)
-    rows = sample_rows(w, n_random=48 if w.S_total <= 65536 else 24)
-    if w.index == 0:
-        rows = np.arange(w.S_local)
-    ref_out, ref_lse = oracle.causal_attention(q, k, v, w.D, r, rows=rows, block=64)
+    ref_out, ref_lse = oracle_rows(q, k, v, w.D, r, rows)
     check(out[:, rows], lse[:, :, rows], ref_out, ref_lse, w.torch_dtype(), C=w.C, rows=rows)
+
+
+@pytest.mark.parametrize("name", ["tiny_zigzag_gqa_f32", "tsp_7b_shard_s32k"])
+def test_fwd_entry_point_direct(name):
+    """tsp_attn_fwd called through the C ABI itself (no binding logic in between) on the
+    tiny fp32 shard in full and the 7B shard on sampled rows, against the oracle; and bit
+    for bit equal to the same attention taken as the key range [0, S_total)."""
+    w = workloads.BY_NAME[name]
+    r = w.ranks[0]
+    _note(f"tsp_attn_fwd direct {name}")
+    q, k, v = workloads.make_inputs(w, r)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((w.B, w.Hq, w.S_local), float("nan"), device=DEV)
+    code = tsp.TSP_BF16 if w.dtype == "bf16" else tsp.TSP_F32
+    stream = torch.cuda.current_stream()
+    st = tsp.lib().tsp_attn_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                w.B, w.S_total, w.D, r, w.Hq, w.Hkv, w.dh, code, stream.cuda_stream)
+    assert st == tsp.TSP_OK, tsp.lib().tsp_attn_last_error()
+    out_r, lse_r = tsp.fwd(qd, kd, vd, D=w.D, rank=r, kv_range=(0, w.S_total))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_r) and torch.equal(lse, lse_r)
+    rows = np.arange(w.S_local) if w.index == 0 else sample_rows(w, n_random=128, edge=16)
+    ref_out, ref_lse = oracle_rows(q, k, v, w.D, r, rows)
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    check(o[:, rows], l[:, :, rows], ref_out, ref_lse, w.torch_dtype(), C=w.C, rows=rows)
 
 
 @pytest.mark.parametrize("rank", range(8))
