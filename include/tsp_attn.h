@@ -193,6 +193,27 @@ int tsp_attn_bwd(const void* q_local, const void* k_full, const void* v_full, co
                  int64_t Hkv, int64_t dh, int dtype, void* stream);
 
 /*
+ * tsp_attn_bwd_noalloc -- tsp_attn_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, but delta (dout_i . out_i per row and head)
+ * lives in a static device array of TSP_BWD_NOALLOC_MAX_ROWS floats (16 MiB) that the
+ * library holds on every GPU it runs on until the process ends, so the call takes no
+ * delta argument and calls no allocator. Arguments, layouts, dtypes and size rules are
+ * those of tsp_attn_bwd, plus B * Hq * 2C <= TSP_BWD_NOALLOC_MAX_ROWS (else TSP_EINVAL,
+ * nothing enqueued). The first call on a device looks the array's address up for that
+ * device (TSP_EINTERNAL if that fails). The array is fully rewritten by every call before
+ * it is read, so nothing carries over from the previous call; but all calls on one GPU
+ * share it: calls that overlap in time on one GPU (other streams, other threads) race and
+ * must be ordered by the caller.
+ */
+#define TSP_BWD_NOALLOC_MAX_ROWS (4 * 1024 * 1024)
+int tsp_attn_bwd_noalloc(const void* q_local, const void* k_full, const void* v_full,
+                         const void* out, const float* lse, const void* dout, void* dq_local,
+                         void* dk_full, void* dv_full, int64_t B, int64_t S_total, int64_t D,
+                         int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
+                         void* stream);
+
+/*
  * Ulysses layout changes around the one-rank (D = 1) attention. DeepSpeed-Ulysses
  * transposes between sequence partitions and head partitions with an all-to-all, so each
  * of P ranks attends over the whole sequence for H/P heads, then transposes back

@@ -32,6 +32,7 @@ TSP_ELAUNCH = -3
 TSP_EINTERNAL = -4
 TSP_BF16 = 0
 TSP_F32 = 1
+MAX_NOALLOC_ROWS = 4 * 1024 * 1024  # TSP_BWD_NOALLOC_MAX_ROWS: B * Hq * 2C of tsp_attn_bwd_noalloc
 
 # Every entry point the header declares, with its ctypes signature.
 _I64 = ctypes.c_int64
@@ -47,6 +48,7 @@ SIGNATURES = {
                                          _VP, ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int, _VP]),
     "tsp_attn_merge": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, ctypes.c_int, _VP]),
     "tsp_attn_bwd": (ctypes.c_int, [_VP] * 10 + [_I64] * 7 + [ctypes.c_int, _VP]),
+    "tsp_attn_bwd_noalloc": (ctypes.c_int, [_VP] * 9 + [_I64] * 7 + [ctypes.c_int, _VP]),
     "tsp_gemm_bf16_nt": (ctypes.c_int, [_VP, _VP, _VP] + [_I64] * 6 + [ctypes.c_int, _VP]),
     "tsp_attn_layer_workspace_bytes": (ctypes.c_int, [_I64] * 8 + [ctypes.POINTER(_I64)]),
     "tsp_attn_layer_fwd": (ctypes.c_int, [_VP] * 7 + [_I64] * 10 + [_VP]),
@@ -306,6 +308,23 @@ def bwd(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, out: 
                                 delta.data_ptr(), B, S_total, D, rank, Hq, Hkv, dh, code, handle)
     _check(st)
     return dq, dk, dv, delta
+
+
+def bwd_noalloc(q_local: torch.Tensor, k_full: torch.Tensor, v_full: torch.Tensor, out: torch.Tensor,
+                lse: torch.Tensor, dout: torch.Tensor, *, D: int, rank: int, dq: torch.Tensor, dk: torch.Tensor,
+                dv: torch.Tensor, stream=None):
+    """The backward through tsp_attn_bwd_noalloc: the caller passes every output (dq, dk,
+    dv) and the library allocates nothing (its delta lives in a static device array of
+    MAX_NOALLOC_ROWS floats per GPU, shared by every call on that GPU). Returns (dq, dk, dv)."""
+    B, S_local, Hq, dh, S_total, Hkv, code = _bwd_check(
+        q_local, k_full, v_full, out, lse, dout, (("dq", dq, q_local), ("dk", dk, k_full), ("dv", dv, v_full)))
+    handle = _handle(stream, q_local.device)
+    with torch.cuda.device(q_local.device):
+        st = lib().tsp_attn_bwd_noalloc(q_local.data_ptr(), k_full.data_ptr(), v_full.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                        B, S_total, D, rank, Hq, Hkv, dh, code, handle)
+    _check(st)
+    return dq, dk, dv
 
 
 def _ulysses_call(fn, src: torch.Tensor, out_shape, B, S_local, H, dh, P, out=None, stream=None):

@@ -1,13 +1,23 @@
 // tsp_attn_bwd.hip -- C ABI of the backward of the per-rank zigzag / GQA causal attention
 // (gfx950): argument validation, work decomposition and dispatch of the three backward
-// kernels (attn_bwd_bf16.h).
+// kernels (attn_bwd_bf16.h); and the allocation-free variant, whose delta lives in a
+// static device array of this file.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 
 #include "tsp_attn.h"
 #include "attn_bwd_bf16.h"
 #include "host_common.h"
 #include "bwd_config.h"
 #include "attn_bwd_f32.h"
+
+// Workspace of the allocation-free entry point: delta (one float per row and query head)
+// in a static device array, one copy per GPU the library runs on, held until the process
+// ends. Host code never passes this name to a kernel: on the host it is only a stand-in,
+// and its device address comes from hipGetSymbolAddress (see scratch_on_current_device).
+constexpr int64_t TSP_BWD_SCRATCH_FLOATS = TSP_BWD_NOALLOC_MAX_ROWS;
+static __device__ __align__(256) float scratch[TSP_BWD_SCRATCH_FLOATS];
 
 namespace {
 
@@ -39,19 +49,48 @@ int kv_block() {
   return 32 * BwdCfg<DH>::KV_NW;
 }
 
-}  // namespace
+// The device address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept; NULL with an error set if the lookup fails.
+float* scratch_on_current_device() {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static float* addr[MAX_DEVICES] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+    fail(TSP_EINTERNAL, "no current HIP device (or device index above %d)", MAX_DEVICES - 1);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(TSP_EINTERNAL, "hipGetSymbolAddress of the backward workspace failed on device %d: %s", dev,
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    addr[dev] = static_cast<float*>(ptr);
+  }
+  return addr[dev];
+}
 
-extern "C" {
-
-int tsp_attn_bwd(const void* q_local, const void* k_full, const void* v_full, const void* out, const float* lse,
-                 const void* dout, void* dq_local, void* dk_full, void* dv_full, float* delta, int64_t B,
-                 int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
-                 void* stream) {
-  const void* ptrs[] = {q_local, k_full, v_full, out, lse, dout, dq_local, dk_full, dv_full, delta};
+// Pointer checks of the backward's inputs and outputs (delta apart).
+int check_bwd_pointers(const void* q_local, const void* k_full, const void* v_full, const void* out,
+                       const float* lse, const void* dout, void* dq_local, void* dk_full, void* dv_full) {
+  const void* ptrs[] = {q_local, k_full, v_full, out, lse, dout, dq_local, dk_full, dv_full};
   for (const void* ptr : ptrs) {
     if (!ptr) return fail(TSP_EINVAL, "null pointer argument");
     if (!aligned16(ptr)) return fail(TSP_EINVAL, "pointers must be 16-byte aligned");
   }
+  return TSP_OK;
+}
+
+// The backward with delta at `delta` (caller's buffer, or the static workspace); pointers
+// already checked. `delta_rows_max` > 0 bounds B * Hq * 2C (the workspace's size).
+int bwd_impl(const void* q_local, const void* k_full, const void* v_full, const void* out, const float* lse,
+             const void* dout, void* dq_local, void* dk_full, void* dv_full, float* delta, int64_t B,
+             int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype, void* stream,
+             int64_t delta_rows_max) {
   int st = tsp_host::check_sizes(S_total, D, rank);
   if (st != TSP_OK) return st;
   if (dtype != TSP_BF16 && dtype != TSP_F32) return fail(TSP_EUNSUPPORTED, "unknown dtype %d", dtype);
@@ -80,6 +119,19 @@ int tsp_attn_bwd(const void* q_local, const void* k_full, const void* v_full, co
   bp.delta = delta;
   bp.n_rows = B * (int64_t)bp.f.S_local * Hq;
   bp.n_kv_rows = B * S_total * Hkv;
+  if (delta_rows_max > 0 && bp.n_rows > delta_rows_max)
+    return fail(TSP_EINVAL, "B * Hq * 2C = %lld rows exceed the static workspace of %lld rows", (long long)bp.n_rows,
+                (long long)delta_rows_max);
+  if (!delta) {  // the static workspace, only now that the sizes are known to fit
+    delta = scratch_on_current_device();
+    if (!delta) return TSP_EINTERNAL;
+    bp.delta = delta;
+  }
+  // every buffer the kernels touch must be set by now (a NULL here would reach the kernels
+  // as a wild address)
+  const void* launch_ptrs[] = {bp.f.q, bp.f.k, bp.f.v, bp.f.out, bp.f.lse, bp.dout, bp.dq, bp.dk, bp.dv, bp.delta};
+  for (const void* ptr : launch_ptrs)
+    if (!ptr) return fail(TSP_EINTERNAL, "backward launch with an unset buffer pointer");
   if (dtype == TSP_F32 && (bp.n_rows > (int64_t(1) << 33) || bp.n_kv_rows > (int64_t(1) << 33)))
     return fail(TSP_EINVAL, "problem too large for the fp32 backward");
   bp.kv_need = (int32_t)((2 * D - rank) * bp.f.C);
@@ -104,6 +156,32 @@ int tsp_attn_bwd(const void* q_local, const void* k_full, const void* v_full, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TSP_ELAUNCH, "backward kernel launch failed: %s", hipGetErrorString(e));
   return tsp_host::ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int tsp_attn_bwd(const void* q_local, const void* k_full, const void* v_full, const void* out, const float* lse,
+                 const void* dout, void* dq_local, void* dk_full, void* dv_full, float* delta, int64_t B,
+                 int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
+                 void* stream) {
+  int st = check_bwd_pointers(q_local, k_full, v_full, out, lse, dout, dq_local, dk_full, dv_full);
+  if (st != TSP_OK) return st;
+  if (!delta) return fail(TSP_EINVAL, "null pointer argument");
+  if (!aligned16(delta)) return fail(TSP_EINVAL, "pointers must be 16-byte aligned");
+  return bwd_impl(q_local, k_full, v_full, out, lse, dout, dq_local, dk_full, dv_full, delta, B, S_total, D, rank, Hq,
+                  Hkv, dh, dtype, stream, 0);
+}
+
+int tsp_attn_bwd_noalloc(const void* q_local, const void* k_full, const void* v_full, const void* out,
+                         const float* lse, const void* dout, void* dq_local, void* dk_full, void* dv_full, int64_t B,
+                         int64_t S_total, int64_t D, int64_t rank, int64_t Hq, int64_t Hkv, int64_t dh, int dtype,
+                         void* stream) {
+  int st = check_bwd_pointers(q_local, k_full, v_full, out, lse, dout, dq_local, dk_full, dv_full);
+  if (st != TSP_OK) return st;
+  return bwd_impl(q_local, k_full, v_full, out, lse, dout, dq_local, dk_full, dv_full, nullptr, B, S_total, D, rank,
+                  Hq, Hkv, dh, dtype, stream, TSP_BWD_SCRATCH_FLOATS);
 }
 
 }  // extern "C"
