@@ -120,6 +120,30 @@ def step_stats(torch, stream, step, n=20):
     return {"median": round(us[n // 2], 1), "min": round(us[0], 1), "n": n}
 
 
+def settle_clocks(torch, stream, step, settle_ms: float):
+    """Untimed launches after the warm-up steps until the GPU has run the step for at least
+    `settle_ms` of its own time since the first of them. From an idle GPU the clocks ramp
+    over the first few tens of milliseconds of load (the 7B-shard forward falls from ~1.2 ms
+    to ~0.94 ms per launch over its first ~40 launches), so a few warm-up steps alone would
+    time the ramp instead of the kernel. Returns what was run, for the JSON line."""
+    if settle_ms <= 0:
+        return {"launches": 0, "ms": 0.0}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1), 1e-3)
+    n = max(0, int(settle_ms / one))
+    e0.record(stream)
+    for _ in range(n):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"launches": n + 1, "ms": round(one + e0.elapsed_time(e1), 1),
+            "why": "untimed, after the warm-up steps: the GPU clocks ramp over the first tens of ms of load"}
+
+
 def balance_bench(args, torch, tsp, workloads):
     """Forward time of several ranks of one workload, each timed like the main benchmark:
     the zigzag split should give every rank the same time."""
@@ -283,6 +307,9 @@ def main():
     ap.add_argument("--workload", default="tsp_7b_shard_s32k")
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="after the warm-up steps, untimed launches until this much GPU time has passed "
+                         "(the clock ramp from idle); 0 disables")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk-pipeline", nargs="?", const="fused", choices=["fused", "merge", "pairs", "ring"],
                     default=None,
@@ -409,6 +436,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    settle = settle_clocks(torch, stream, step, args.settle_ms)
 
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -475,6 +503,7 @@ def main():
             "kernel_ms": round(kernel_ms, 4),
         },
         "step_us": launch,
+        "settle": settle,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
