@@ -35,6 +35,13 @@
 #include "attn_common.h"
 #include "attn_fwd_bf16.h"
 
+#ifndef TSP_BWD_UNROLL_RING_PIPE
+#define TSP_BWD_UNROLL_RING_PIPE 1
+#endif
+#ifndef TSP_BWD_UNROLL_RING_NOPIPE
+#define TSP_BWD_UNROLL_RING_NOPIPE 1
+#endif
+
 namespace tsp {
 
 typedef float tsp_f32x4 __attribute__((ext_vector_type(4)));
@@ -165,6 +172,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
   constexpr bool DO_DV = MODE != BWD_KV_DK, DO_DK = MODE != BWD_KV_DV;
   constexpr int NDB = DH / 32, NKK = DH / 16, PD = NBUF - 1, KB = 32 * NW;
   constexpr int VM_STAGE = T::LPW + 1;  // loads per wave per stage (tiles + metadata)
+  // unroll the step loop over whole ring cycles (constant LDS slots) where the registers allow
+  constexpr bool UNROLL_RING = DH <= 128 && (PIPE ? TSP_BWD_UNROLL_RING_PIPE : TSP_BWD_UNROLL_RING_NOPIPE);
   static_assert(PD >= 2 && VM_STAGE * (PD - 1) < 64, "ring depth / vmcnt range");
   const TspParams& p = bp.f;
 
@@ -256,7 +265,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
   const uint16_t* __restrict__ dog = static_cast<const uint16_t*>(bp.dout);
 
-  auto issue = [&](int u) {
+  auto issue = [&](int u) __attribute__((always_inline)) {
     const uint32_t base = smem_addr + (u % NBUF) * T::STAGE_BYTES;  // the slot of stage u
     u = min(u, n_steps - 1);  // past the end: a duplicate of the last stage into that free slot
     const int32_t hl = u / tiles;
@@ -287,10 +296,24 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
 
   const int32_t wave_key_max = j0 + 32 * wave + 31;
 
-  // S = Q K^T and dP = dO V^T of step t: lane holds key `col`, query rows
+  // Every stage is addressed through its slot's base pointer: the loop below is unrolled
+  // over the ring, so for most steps the slot is a constant folded into the LDS
+  // instructions' offsets instead of an address add per read.
+  auto slot = [&](int t) __attribute__((always_inline)) { return smem + (t % NBUF) * T::STAGE_BYTES; };
+
+  // The wave's metadata of a stage holds lse (lanes 0..31) then Delta (lanes 32..63) of the
+  // tile's rows; once the stage has landed the wave turns its lse values into
+  // -lse * log2(e), the exponent offset of the weights (one multiply per stage instead of
+  // one per weight).
+  const float meta_scale = half ? 1.0f : -TSP_LOG2E;
+  auto prescale_meta = [&](const uint8_t* qs) __attribute__((always_inline)) {
+    float* m = reinterpret_cast<float*>(const_cast<uint8_t*>(qs) + 2 * T::TILE_BYTES + wave * T::META_BYTES) + lane;
+    *m = *m * meta_scale;
+  };
+
+  // S = Q K^T and dP = dO V^T of the stage at qs: lane holds key `col`, query rows
   // 8(e/4) + 4*half + e%4 of the step's tile
-  auto sdp = [&](int t, tsp_f32x16& s, tsp_f32x16& dp) {
-    const uint8_t* qs = smem + (t % NBUF) * T::STAGE_BYTES;
+  auto sdp = [&](const uint8_t* qs, tsp_f32x16& s, tsp_f32x16& dp) __attribute__((always_inline)) {
     const uint8_t* ds = qs + T::TILE_BYTES;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -313,35 +336,38 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
 
   // P = exp2(s * log2(e)/sqrt(dh) - lse * log2(e)) on visible pairs, dS = P (dP - Delta),
   // then dV^T += dO^T P and dK^T += Q^T dS (rows = dims, columns = keys)
-  auto grads = [&](int t, const tsp_f32x16& s, const tsp_f32x16& dp) {
-    const uint8_t* qs = smem + (t % NBUF) * T::STAGE_BYTES;
+  auto grads = [&](int t, const uint8_t* qs, const tsp_f32x16& s, const tsp_f32x16& dp) __attribute__((always_inline)) {
     const uint8_t* ds = qs + T::TILE_BYTES;
     const float* meta = reinterpret_cast<const float*>(qs + 2 * T::TILE_BYTES + wave * T::META_BYTES);
     const int32_t i0 = (t_first + t % tiles) * 32;
     const int32_t pos0 = tsp_zigzag_position(i0, C, p.D, p.rank);
     const bool irregular = i0 + 31 >= p.S_local || (i0 < C && i0 + 31 >= C);
-    // exponent arguments of the lane's 16 rows
+    // exponent arguments of the lane's 16 rows (the metadata holds -lse * log2(e))
     float x[16], del[16];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const tsp_f32x4 lse4 = *reinterpret_cast<const tsp_f32x4*>(meta + 8 * a + 4 * half);
+      const tsp_f32x4 nl4 = *reinterpret_cast<const tsp_f32x4*>(meta + 8 * a + 4 * half);
       const tsp_f32x4 del4 = *reinterpret_cast<const tsp_f32x4*>(meta + 32 + 8 * a + 4 * half);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[4 * a + e] = fmaf(s[4 * a + e], p.scale_log2, -lse4[e] * TSP_LOG2E);
+        x[4 * a + e] = fmaf(s[4 * a + e], p.scale_log2, nl4[e]);
         del[4 * a + e] = del4[e];
       }
     }
     // causal mask (steps that reach past a row's position, and irregular tiles that hold
-    // a chunk boundary or rows past the last): masked arguments become -inf, weight 0
-    if (irregular) {
+    // a chunk boundary or rows past the last): masked arguments become -inf, weight 0. Both
+    // cases are rare, wave-uniform branches; the empty asm keeps the compiler from turning
+    // them into selects executed on every step.
+    if (__builtin_expect(irregular, 0)) {
+      asm volatile("");
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int32_t row = i0 + 8 * (v >> 2) + 4 * half + (v & 3);
         const int32_t pos = tsp_zigzag_position(min(row, p.S_local - 1), C, p.D, p.rank);
         if (row >= p.S_local || key > pos) x[v] = -INFINITY;
       }
-    } else if (wave_key_max > pos0) {
+    } else if (__builtin_expect(wave_key_max > pos0, 0)) {
+      asm volatile("");
       const int32_t lim = key - pos0 - 4 * half;  // row offsets below this see no key
 #pragma unroll
       for (int v = 0; v < 16; ++v)
@@ -378,41 +404,62 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
       }
   };
 
-  // Step t: the S / dP products of step t+1 go to the matrix pipe ahead of step t's VALU
-  // work, then step t's dV / dK products. Stages t and t+1 are read in step t, so the
+  // Step t (PIPE): the S / dP products of step t+1 go to the matrix pipe ahead of step t's
+  // VALU work, then step t's dV / dK products. Stages t and t+1 are read in step t, so the
   // stage issued here, NBUF-1 ahead, takes the slot of stage t-1.
-  auto step = [&](int t, tsp_f32x16& sc, tsp_f32x16& dc, tsp_f32x16& sn, tsp_f32x16& dn) {
+  auto step = [&](int t, const uint8_t* cur, const uint8_t* nxt, tsp_f32x16& sc, tsp_f32x16& dc, tsp_f32x16& sn,
+                  tsp_f32x16& dn) __attribute__((always_inline)) {
     tsp_wait_vm<VM_STAGE * (PD - 2)>();  // stage t+1 landed (this wave's part)
     __syncthreads();                     // ... for every wave; every wave is past step t-1
+    prescale_meta(nxt);
     issue(t + PD);
-    sdp(t + 1, sn, dn);  // past the last step this reads a duplicate stage; unused
-    grads(t, sc, dc);
+    sdp(nxt, sn, dn);  // past the last step this reads a duplicate stage; unused
+    grads(t, cur, sc, dc);
+  };
+  // Step t without the pipeline: one stage per step.
+  auto step1 = [&](int t, const uint8_t* cur) __attribute__((always_inline)) {
+    tsp_wait_vm<VM_STAGE * (PD - 1)>();  // stage t landed (this wave's part)
+    __syncthreads();                     // ... for every wave; the slot of stage t-1 is free
+    prescale_meta(cur);
+    issue(t + PD);
+    tsp_f32x16 s0, d0;
+    sdp(cur, s0, d0);
+    grads(t, cur, s0, d0);
   };
 
 #pragma unroll 1
   for (int u = 0; u < PD; ++u) issue(u);
+  static_assert(NBUF % 2 == 0, "the unrolled groups keep the two score tiles' roles");
   if constexpr (PIPE) {
     tsp_wait_vm<VM_STAGE * (PD - 1)>();
     __syncthreads();
+    prescale_meta(smem);
     tsp_f32x16 s0, d0, s1, d1;
-    sdp(0, s0, d0);
+    sdp(smem, s0, d0);
     int t = 0;
+    // whole ring cycles: the slots are compile-time constants
+#pragma unroll 1
+    for (; UNROLL_RING && t + NBUF <= n_steps; t += NBUF)
+      [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
+        ((Us % 2 == 0 ? step(t + Us, smem + Us * T::STAGE_BYTES, smem + ((Us + 1) % NBUF) * T::STAGE_BYTES, s0, d0, s1, d1)
+                      : step(t + Us, smem + Us * T::STAGE_BYTES, smem + ((Us + 1) % NBUF) * T::STAGE_BYTES, s1, d1, s0, d0)),
+         ...);
+      }(std::make_integer_sequence<int, NBUF>{});
 #pragma unroll 1
     for (; t + 2 <= n_steps; t += 2) {
-      step(t, s0, d0, s1, d1);
-      step(t + 1, s1, d1, s0, d0);
+      step(t, slot(t), slot(t + 1), s0, d0, s1, d1);
+      step(t + 1, slot(t + 1), slot(t + 2), s1, d1, s0, d0);
     }
-    if (t < n_steps) step(t, s0, d0, s1, d1);
+    if (t < n_steps) step(t, slot(t), slot(t + 1), s0, d0, s1, d1);
   } else {
+    int t = 0;
 #pragma unroll 1
-    for (int t = 0; t < n_steps; ++t) {
-      tsp_wait_vm<VM_STAGE * (PD - 1)>();  // stage t landed (this wave's part)
-      __syncthreads();                     // ... for every wave; the slot of stage t-1 is free
-      issue(t + PD);
-      tsp_f32x16 s0, d0;
-      sdp(t, s0, d0);
-      grads(t, s0, d0);
-    }
+    for (; UNROLL_RING && t + NBUF <= n_steps; t += NBUF)
+      [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
+        (step1(t + Us, smem + Us * T::STAGE_BYTES), ...);
+      }(std::make_integer_sequence<int, NBUF>{});
+#pragma unroll 1
+    for (; t < n_steps; ++t) step1(t, slot(t));
   }
   tsp_wait_vm<0>();  // the trailing duplicate loads land before the workgroup ends
 
