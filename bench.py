@@ -35,17 +35,24 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 FORWARD_SOURCES = ("csrc/attn_common.h", "csrc/attn_fwd_bf16.h", "csrc/zigzag.h", "csrc/host_common.h",
                    "csrc/tsp_attn_fwd_bf16.hip", "csrc/tsp_attn.hip")
 FORWARD_UNIT = "tsp_attn_fwd_bf16.hip"
+# the same for the backward kernels of dh <= 128 (the bench workload's backward)
+BACKWARD_SOURCES = ("csrc/attn_common.h", "csrc/attn_fwd_bf16.h", "csrc/attn_bwd_bf16.h", "csrc/bwd_config.h",
+                    "csrc/zigzag.h", "csrc/host_common.h", "csrc/tsp_attn_bwd.hip")
+BACKWARD_UNIT = "tsp_attn_bwd.hip"
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(backward: bool = False) -> str:
+    """A short hash of the kernel sources and the compile flags of their unit, which ties
+    a profile summary to the code it was taken on (the forward's, or the backward's)."""
     from sequence_causal_attention_amd import build as b
 
     pkg = os.path.join(ROOT, "sequence_causal_attention_amd")
     h = hashlib.sha256()
-    for name in FORWARD_SOURCES:
+    for name in BACKWARD_SOURCES if backward else FORWARD_SOURCES:
         with open(os.path.join(pkg, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
-    flags = [fl for src, fl in b.UNITS if os.path.basename(src) == FORWARD_UNIT]
+    unit = BACKWARD_UNIT if backward else FORWARD_UNIT
+    flags = [fl for src, fl in b.UNITS if os.path.basename(src) == unit]
     h.update(repr((b.COMMON, flags)).encode())
     return h.hexdigest()[:16]
 

@@ -166,10 +166,15 @@ struct BwdQTile {
 // MFMA work (S is computed twice).
 enum BwdKvMode : int { BWD_KV_BOTH = 0, BWD_KV_DV = 1, BWD_KV_DK = 2 };
 
-template <int DH, int NW, int NBUF, bool PIPE, int MODE, int OCC>
+// VLDS (both gradients only): each lane parks its key's V row in LDS instead of registers
+// (NKK x 16 bytes per lane, laid out lane-linear, read back by the same lane only), which
+// brings the one-launch kernel down to the registers of two waves per SIMD.
+template <int DH, int NW, int NBUF, bool PIPE, int MODE, int OCC, bool VLDS = false>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdParams bp) {
   using T = BwdQTile<DH, NW>;
   constexpr bool DO_DV = MODE != BWD_KV_DK, DO_DK = MODE != BWD_KV_DV;
+  static_assert(!VLDS || MODE == BWD_KV_BOTH, "V in LDS is for the one-launch kernel");
+  constexpr int VL_BYTES = VLDS ? NW * (DH / 16) * 1024 : 0;  // the parked V rows
   constexpr int NDB = DH / 32, NKK = DH / 16, PD = NBUF - 1, KB = 32 * NW;
   constexpr int VM_STAGE = T::LPW + 1;  // loads per wave per stage (tiles + metadata)
   // unroll the step loop over whole ring cycles (constant LDS slots) where the registers allow
@@ -177,13 +182,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
   static_assert(PD >= 2 && VM_STAGE * (PD - 1) < 64, "ring depth / vmcnt range");
   const TspParams& p = bp.f;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * T::STAGE_BYTES + VL_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int half = lane >> 5;
+  // this lane's parked V row: 16 bytes per reduction step kk at vls + 1024 * kk
+  uint8_t* const vls = smem + NBUF * T::STAGE_BYTES + wave * (DH / 16) * 1024 + lane * 16;
 
   int32_t unit = tsp_xcd_unit(blockIdx.x, gridDim.x);
   const int32_t kblk = unit % bp.n_kblocks;
@@ -220,7 +227,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       kf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(kp + 16 * kk));
-      if constexpr (DO_DK) vf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(vp + 16 * kk));
+      if constexpr (VLDS) *reinterpret_cast<tsp_u32x4*>(vls + 1024 * kk) = *reinterpret_cast<const tsp_u32x4*>(vp + 16 * kk);
+      else if constexpr (DO_DK) vf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(vp + 16 * kk));
     }
   }
 
@@ -329,7 +337,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const tsp_bf16x8 da = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(ds + qoff[kk]));
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
+        const tsp_bf16x8 vb =
+            VLDS ? __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(vls + 1024 * kk)) : vf[kk];
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, dp, 0, 0, 0);
       }
     }
   };
@@ -429,7 +439,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
 
 #pragma unroll 1
   for (int u = 0; u < PD; ++u) issue(u);
-  static_assert(NBUF % 2 == 0, "the unrolled groups keep the two score tiles' roles");
+  static_assert(!PIPE || NBUF % 2 == 0, "the unrolled groups keep the two score tiles' roles");
   if constexpr (PIPE) {
     tsp_wait_vm<VM_STAGE * (PD - 1)>();
     __syncthreads();

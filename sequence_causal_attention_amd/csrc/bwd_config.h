@@ -32,6 +32,15 @@
 #ifndef TSP_BWD_KV_SPLIT
 #define TSP_BWD_KV_SPLIT 1
 #endif
+#ifndef TSP_BWD_KV_FUSED
+#define TSP_BWD_KV_FUSED 1
+#endif
+#ifndef TSP_BWD_KV_NW_FUSED
+#define TSP_BWD_KV_NW_FUSED 8
+#endif
+#ifndef TSP_BWD_KV_NBUF_FUSED
+#define TSP_BWD_KV_NBUF_FUSED 4
+#endif
 template <int DH>
 struct BwdCfg {
   static constexpr int KV_NW = 4, KV_NBUF = DH <= 128 ? TSP_BWD_KV_NBUF : 4;
@@ -41,6 +50,9 @@ struct BwdCfg {
   static constexpr bool KV_PIPE_DV = DH <= 128 && TSP_BWD_KV_PIPE_DV, KV_PIPE_DK = DH <= 128 && TSP_BWD_KV_PIPE_DK;
   // dK and dV in separate launches at two waves per SIMD (dh <= 128), or one launch
   static constexpr bool KV_SPLIT = DH <= 128 && TSP_BWD_KV_SPLIT;
+  // dK and dV in one launch at two waves per SIMD, V parked in LDS (dh <= 128)
+  static constexpr bool KV_FUSED = DH <= 128 && TSP_BWD_KV_FUSED;
+  static constexpr int KV_NW_FUSED = TSP_BWD_KV_NW_FUSED, KV_NBUF_FUSED = TSP_BWD_KV_NBUF_FUSED;
   static constexpr int Q_NW = DH <= 128 ? TSP_BWD_Q_NW : 4, Q_NBUF = 4, Q_OCC = DH <= 128 ? 2 : 1;
 };
 
@@ -54,7 +66,14 @@ void tsp_bwd_launch(const tsp::TspBwdParams& bp, int64_t kv_units, hipStream_t s
                      s, bp);
   hipLaunchKernelGGL((tsp::attn_bwd_dq_bf16_kernel<DH, C::Q_NW, C::Q_NBUF, C::Q_OCC>), dim3(bp.f.n_units),
                      dim3(C::Q_NW * 64), 0, s, bp);
-  if constexpr (C::KV_SPLIT) {
+  if constexpr (C::KV_FUSED) {
+    tsp::TspBwdParams bf = bp;
+    bf.n_kblocks = (bp.f.S_total + 32 * C::KV_NW_FUSED - 1) / (32 * C::KV_NW_FUSED);
+    const int64_t f_units = kv_units / bp.n_kblocks * bf.n_kblocks;
+    hipLaunchKernelGGL(
+        (tsp::attn_bwd_dkv_bf16_kernel<DH, C::KV_NW_FUSED, C::KV_NBUF_FUSED, false, tsp::BWD_KV_BOTH, 2, true>),
+        dim3((unsigned)f_units), dim3(C::KV_NW_FUSED * 64), 0, s, bf);
+  } else if constexpr (C::KV_SPLIT) {
     // the dV launch may own more keys per workgroup: its own key blocks
     tsp::TspBwdParams bv = bp;
     bv.n_kblocks = (bp.f.S_total + 32 * C::KV_NW_DV - 1) / (32 * C::KV_NW_DV);
