@@ -130,7 +130,10 @@ def test_ring_reads_chunks_only_after_they_arrive():
     launch runs: the peers' chunks start as NaN on the device and each chunk's flag is
     copied in after its data, so a chunk read before its flag would put NaN into the
     result. The launch is enqueued first and the copies only afterwards (a host pause in
-    between), so its waits see the flags arrive."""
+    between), so its waits see the flags arrive. The spin budget (2^22 polls of ~1 us, some
+    seconds per wait) lies far above any copy time, so the outcome does not depend on how
+    fast the box delivers the copies; a wait that did give up would be reported through
+    the status word, never hang."""
     import time
 
     B, S, D, r, Hq, Hkv, dh = 1, 4096, 4, 3, 4, 2, 128
@@ -153,7 +156,7 @@ def test_ring_reads_chunks_only_after_they_arrive():
         torch.empty_like(kd[:, :C]).copy_(k_host[:, :C], non_blocking=True)
     torch.cuda.synchronize()
     with torch.cuda.stream(compute):
-        out, lse = tsp.fwd_ring(qd, kd, vd, D=D, rank=r, chunk_ready=ready, ready_value=1, spin_limit=1 << 19,
+        out, lse = tsp.fwd_ring(qd, kd, vd, D=D, rank=r, chunk_ready=ready, ready_value=1, spin_limit=1 << 22,
                                 wait_status=status, stream=compute)
     time.sleep(0.005)
     with torch.cuda.stream(comm):
