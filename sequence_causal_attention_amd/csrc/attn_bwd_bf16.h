@@ -15,8 +15,8 @@
 // Three kernels, no atomics and no scratch buffer:
 //  * attn_bwd_delta_kernel: Delta_i, one fp32 per (row, head) from the bf16 O and dO.
 //  * attn_bwd_dkv_bf16_kernel (key-stationary): a workgroup owns 32*NW keys of one KV
-//    head, each wave 32 of them, with its K and V rows as MFMA B operands in registers.
-//    It sweeps the 32-row tiles of Q and dO (every query head of the group, every tile
+//    head, each wave 32 of them, with its K and V rows as MFMA B operands in registers
+//    (or, in the one-launch form at dh <= 128, its V rows parked in LDS). It sweeps the 32-row tiles of Q and dO (every query head of the group, every tile
 //    whose rows see the keys) through an LDS ring. Scores are computed as S = Q K^T, with
 //    queries on MFMA rows and keys on columns: each lane holds one key, so P and dS,
 //    rounded to bf16, are directly the B operands of dV^T += dO^T P and dK^T += Q^T dS,
@@ -160,10 +160,11 @@ struct BwdQTile {
 
 // PIPE: issue the next step's S / dP products ahead of the current step's VALU work (one
 // more score tile live; off where the registers do not allow it).
-// MODE: which gradients one launch computes. Both (S, dP, P, dS, dV and dK) need about 300
-// registers per lane at dh 128, one wave per SIMD; dV alone (S, P, dV) and dK alone (S,
-// dP, P, dS, dK) each fit in 256, so two launches run at two waves per SIMD for 25% more
-// MFMA work (S is computed twice).
+// MODE: which gradients one launch computes. Both (S, dP, P, dS, dV and dK) with K and V in
+// registers need about 300 registers per lane at dh 128, one wave per SIMD; with V parked
+// in LDS (VLDS) they fit in 256, two waves per SIMD, the form used at dh <= 128. dV alone
+// (S, P, dV) and dK alone (S, dP, P, dS, dK) also fit in 256 with K and V in registers, as
+// two launches that compute S twice.
 enum BwdKvMode : int { BWD_KV_BOTH = 0, BWD_KV_DV = 1, BWD_KV_DK = 2 };
 
 // VLDS (both gradients only): each lane parks its key's V row in LDS instead of registers

@@ -48,7 +48,8 @@ struct BwdCfg {
   static constexpr int KV_NW_DK = DH <= 128 ? TSP_BWD_KV_NW_DK : KV_NW;  // waves of the dK launch
   static constexpr bool KV_PIPE = DH <= 128 && TSP_BWD_KV_PIPE;
   static constexpr bool KV_PIPE_DV = DH <= 128 && TSP_BWD_KV_PIPE_DV, KV_PIPE_DK = DH <= 128 && TSP_BWD_KV_PIPE_DK;
-  // dK and dV in separate launches at two waves per SIMD (dh <= 128), or one launch
+  // with the one-launch form off: dK and dV in separate launches at two waves per SIMD
+  // (dh <= 128), or one launch at one wave per SIMD
   static constexpr bool KV_SPLIT = DH <= 128 && TSP_BWD_KV_SPLIT;
   // dK and dV in one launch at two waves per SIMD, V parked in LDS (dh <= 128)
   static constexpr bool KV_FUSED = DH <= 128 && TSP_BWD_KV_FUSED;
