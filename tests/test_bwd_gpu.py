@@ -104,10 +104,13 @@ def test_bwd_workload_sampled_heads():
     check_grad("dv", _np(dv[:, :, heads]), rv, 2)
 
 
-def test_bwd_closed_form_sums_full_size():
+@pytest.mark.parametrize("name", ["gqa_shard_s64k", "ulysses_head_subset_s128k", "tsp_7b_shard_s32k"])
+def test_bwd_closed_form_sums_full_size(name):
     """At full size, for every KV head: dK sums to 0 over the keys and dV sums to the
-    group's total dout (softmax rows sum to 1); keys past the rank's last position are 0."""
-    w = workloads.BY_NAME["gqa_shard_s64k"]
+    group's total dout (softmax rows sum to 1); keys past the rank's last position are 0.
+    Covers the one-wave dh-256 kernel (GQA shard) and the two-wave one-launch dK/dV kernel
+    at D = 1 (Ulysses shard, 131072 keys) and on the 7B shard."""
+    w = workloads.BY_NAME[name]
     r = w.ranks[0]
     _note(f"bwd sums {w.name}")
     q, k, v = workloads.make_inputs(w, r)
