@@ -22,7 +22,7 @@ What it computes (the plain definition, written out step by step):
   and the sequence-parallel paragraph: Ulysses gives each rank full attention over a
   subset of heads, which is the one-rank (D = 1) case here.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * zigzag map: the sequence is cut into 2D equal chunks of C = S_total / (2D) tokens and
   rank r holds chunk r followed by chunk 2D-1-r (local rows [0, C) then [C, 2C));

@@ -14,7 +14,7 @@ the standard causal multi-head (grouped-query) attention layer:
 where K, V hold every token's projections at its global position (the rank's own rows
 x W_K^T, x W_V^T; the other rows those of the other ranks).
 
-Readings (listed in DESIGN.md too): weights in the [out_features, in_features] layout;
+Readings: weights in the [out_features, in_features] layout;
 w_qkv stacks the rows of W_Q (query heads in order), W_K and W_V; shard i holds query
 heads i*Hq/D .. and KV heads i*Hkv/D .. (whole heads per shard, so Hq and Hkv divide by
 D); no bias; the attention is this package's oracle attention (zigzag positions, GQA,

@@ -13,7 +13,7 @@ What is computed:
   sequence for a subset of heads, MLP buffers a part of the sequence for the whole model
   width; item 3 (communication insertion): all-to-all at the boundaries of attention.
 
-Readings taken where the pages are silent (listed in the design doc too):
+Readings taken where the pages are silent:
 
 * P ranks; before attention rank p holds the contiguous sequence chunk p of S_local
   tokens, [B, S_local, H, dh], all heads;
