@@ -34,6 +34,13 @@
 //    reach past a wave's first position apply the element mask (key > position -> -inf).
 //  * Online softmax in base 2 (log2(e)/sqrt(dh) folded into one FMA), running max raised
 //    lazily (TSP_RESCALE_SLACK), row sums from the rounded bf16 weights (v_dot2).
+//  * dh 256 runs one wave per SIMD (its Q^T operands and output fill the registers), so
+//    no second wave covers a wave's own waits. Its unrolled steps keep the running max of
+//    the sweep's first step (no per-step test and branch; a tile that overflowed is swept
+//    again with the test) and are issued in a fixed order: K operands read four products
+//    ahead, the V^T operands and the weights of step t under the QK^T products of step
+//    t+1, then the PV products back to back with the stage boundary and the next loads
+//    under them.
 #pragma once
 
 #include <type_traits>
@@ -148,6 +155,12 @@ struct Bf16Stage {
 // position, so nothing is masked). The sweep runs over a virtual key axis (the visible
 // chunks back to back); each stage's physical keys come from the chunk cursor, which also
 // waits for the chunk's arrival flag before the first stage of a chunk is loaded.
+#ifndef TSP_FWD_FIXED_MAX
+#define TSP_FWD_FIXED_MAX 1
+#endif
+#ifndef TSP_FWD_PINNED
+#define TSP_FWD_PINNED 1
+#endif
 template <int DH, int NW, int RB, int NBUF, int SPS, int OCC, int NR>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p) {
   using St = Bf16Stage<DH, NW, NBUF, SPS>;
@@ -155,6 +168,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
   constexpr int NDB = DH / 32;  // 32-dim blocks of the output
   constexpr int NKK = DH / 16;  // reduction steps of QK^T
   constexpr int PD = St::PD;
+  // dh 256 (one wave per SIMD, where the per-step test costs most): the unrolled steps keep
+  // the running max of their first step instead of testing every step's scores against it.
+  // Their weights are then 2^(x - m) with m at most the row's true max, exact up to overflow;
+  // a tile whose sums or outputs left the finite range is swept again with the test on
+  // every step.
+  constexpr bool FIXED_MAX = DH == 256 && NR != 3 && TSP_FWD_FIXED_MAX;
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * St::STAGE_BYTES];
 
@@ -182,21 +201,25 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
   const int pos_blocks = p.BQ / 32;  // row blocks per head in a tile
 
   // ---- per-lane LDS read offsets (constant over the sweep) ------------------------------
-  // K operand of QK^T step kk: row `col`, logical chunk 2kk + half.
-  int koff[NKK];
+  // K operand of QK^T step kk: row `col`, logical chunk 2kk + half. With FIXED_MAX (its
+  // registers are short), one offset per swizzle period: chunks SWZ apart lie SWZ * 16
+  // bytes apart, so KP (VP) offsets serve all NKK (NDB) operands.
+  constexpr int KP = FIXED_MAX && NKK > St::SWZ / 2 ? St::SWZ / 2 : NKK;
+  constexpr int VP = FIXED_MAX && NDB > St::SWZ / 4 ? St::SWZ / 4 : NDB;
+  int koff[KP];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) koff[kk] = col * St::ROW_BYTES + (((2 * kk + half) ^ St::swz_k(col)) << 4);
+  for (int kk = 0; kk < KP; ++kk) koff[kk] = col * St::ROW_BYTES + (((2 * kk + half) ^ St::swz_k(col)) << 4);
   // V^T operand of PV block db: in each 16-lane group g, source lane s addresses row
   // 4*half + s/4 (+16 per 16-key step, +8 for the second read) and dims
   // db*32 + 16(g&1) + 4(s&3) .. +3; lane s then receives dim db*32 + 16(g&1) + s of the
   // 4 rows, which is the A operand layout with keys in the P operand's order.
-  int voff[NDB];
+  int voff[VP];
   {
     const int g = lane >> 4, s = lane & 15;
     const int vrow = 4 * half + (s >> 2);
     const int xv = St::swz_v(vrow);  // rows +8 and +16 have the same swizzle
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < VP; ++db) {
       const int chunk = db * 4 + 2 * (g & 1) + ((s & 3) >> 1);
       voff[db] = St::V_BASE + vrow * St::ROW_BYTES + ((chunk ^ xv) << 4) + ((s & 1) << 3);
     }
@@ -473,7 +496,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       tsp_bf16x8 kf[NKK];  // all K operands of the step in flight before the first MFMA
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
-        kf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(kt + koff[kk]));
+        kf[kk] = __builtin_bit_cast(tsp_bf16x8,
+                                    *reinterpret_cast<const tsp_u32x4*>(kt + koff[kk % KP] + (kk / KP) * St::SWZ * 16));
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
@@ -580,7 +604,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const uint8_t* a = vt + voff[db] + st * 16 * St::ROW_BYTES;
+          const uint8_t* a = vt + voff[db % VP] + (db / VP) * St::SWZ * 16 + st * 16 * St::ROW_BYTES;
           const tsp_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a));
           const tsp_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a + 8 * St::ROW_BYTES));
           const tsp_bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -591,119 +615,248 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       }
     };
 
-    // ---- prologue -------------------------------------------------------------------
-    __syncthreads();  // the previous tile's readers are done with every buffer
-    const int pro = min(PD, n_stage - 1);
-    for (int s = 0; s <= pro; ++s) issue_stage(s);
-    stage_ready(0, pro);
-
-    tsp_f32x16 s_cur[RB];
-    float mx[RB];
-    qk(0, s_cur);
-    if (needs_mask(0)) mask(0, s_cur);
-    rowmax(s_cur, mx);
-
-    // ---- main sweep ----------------------------------------------------------------------
-    // Fast path: steps whose successor needs no mask and whose prefetched stage lies fully
-    // below the end of its range. Unrolled over whole ring cycles so every LDS slot is a compile-time
-    // offset and the two score tiles alternate without copies; constant vmcnt; no clamping.
-    constexpr int VM_STEADY = St::LPW * (PD - 1);
-    static_assert(VM_STEADY < 16, "vmcnt immediate");
-    constexpr int GROUP = (NBUF * SPS) % 2 == 0 ? NBUF * SPS : 2 * NBUF * SPS;  // steps per unrolled group
-    int32_t n_full = kv_end / St::BKS;  // stages with every key below the end of their range
-    int32_t t_unmasked = t_mask;        // the steps from u_left up to it need no mask
-    if constexpr (NR == 2) {
-      if (run_on) {
-        n_full = n_stage1 + kv_end2 / St::BKS;
-        t_unmasked = T1 + t_mask2;
+    for (int attempt = 0;; ++attempt) {  // a second sweep only after an overflow (FIXED_MAX)
+      if (attempt > 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          m_run[rb] = -INFINITY;
+          m_thr[rb] = -INFINITY;
+          l_run[rb] = 0.f;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[rb][db][e] = 0.f;
+        }
       }
-    }
-    const int t_fast = u_left == 0 ? min(t_unmasked - 1, (n_full - PD) * SPS - 1) : 0;
-    tsp_f32x16 s_alt[RB];
-    // Stage boundary: wait until stage NEXT (relative to t0 / SPS) landed for every wave,
-    // then issue the stage PD ahead into the slot two stages back.
-    auto boundary = [&](auto next_const, int t0) {
-      constexpr int NEXT = decltype(next_const)::value;
-      __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // that stage landed (this wave's part)
-      __syncthreads();  // ... for every wave; the slot two stages back is free again
-      const int32_t sg = t0 / SPS + NEXT + PD;  // the stage to issue
-      int64_t adv = (int64_t)sg * stage_stride;
-      if constexpr (NR == 3) adv = (int64_t)ring_stage_key(sg) * kv_row_stride;
-      const uint16_t* kb = kbase;
-      const uint16_t* vb = vbase;
+      // ---- prologue -------------------------------------------------------------------
+      __syncthreads();  // the previous tile's readers are done with every buffer
+      const int pro = min(PD, n_stage - 1);
+      for (int s = 0; s <= pro; ++s) issue_stage(s);
+      stage_ready(0, pro);
+
+      tsp_f32x16 s_cur[RB];
+      float mx[RB];
+      qk(0, s_cur);
+      if (needs_mask(0)) mask(0, s_cur);
+      rowmax(s_cur, mx);
+      if constexpr (FIXED_MAX) {
+        if (rescale_needed(mx)) rescale(mx);  // the running max the unrolled steps keep
+      }
+
+      // ---- main sweep ----------------------------------------------------------------------
+      // Fast path: steps whose successor needs no mask and whose prefetched stage lies fully
+      // below the end of its range. Unrolled over whole ring cycles so every LDS slot is a compile-time
+      // offset and the two score tiles alternate without copies; constant vmcnt; no clamping.
+      constexpr int VM_STEADY = St::LPW * (PD - 1);
+      static_assert(VM_STEADY < 16, "vmcnt immediate");
+      constexpr int GROUP = (NBUF * SPS) % 2 == 0 ? NBUF * SPS : 2 * NBUF * SPS;  // steps per unrolled group
+      int32_t n_full = kv_end / St::BKS;  // stages with every key below the end of their range
+      int32_t t_unmasked = t_mask;        // the steps from u_left up to it need no mask
       if constexpr (NR == 2) {
-        if (sg >= n_stage1) {  // a stage of the second range
-          kb = kbase2;
-          vb = vbase2;
-          adv -= stage_off2;
+        if (run_on) {
+          n_full = n_stage1 + kv_end2 / St::BKS;
+          t_unmasked = T1 + t_mask2;
         }
       }
-      const uint32_t base = smem_addr + ((NEXT + PD) % NBUF) * St::SLOT_STRIDE;
-#pragma unroll
-      for (int q = 0; q < St::LPW; ++q)
-        tsp_lds_dma16((dma_isv[q] ? vb : kb) + adv, dma_voff[q], base + dma_slot[q]);
-    };
-    // LAG (second half of the waves, one of the two waves of each SIMD): the barrier of
-    // stage k comes after the PV products of step SPS*k - 2 instead of before the QK
-    // products of step SPS*k - 1. Every barrier still precedes the first read of its stage
-    // and follows the last read of the stage two back, but the two waves of a SIMD then run
-    // their matrix and vector phases in alternation (one's softmax under the other's MFMAs).
-    auto fast_step = [&](auto u_const, auto lag_const, int t0) {
-      constexpr int U = decltype(u_const)::value;  // step t = t0 + U, t0 a multiple of GROUP
-      constexpr bool LAG = decltype(lag_const)::value;
-      tsp_f32x16(&sc)[RB] = (U % 2 == 0) ? s_cur : s_alt;
-      tsp_f32x16(&sn)[RB] = (U % 2 == 0) ? s_alt : s_cur;
-      if (rescale_needed(mx)) rescale(mx);
-      if constexpr (!LAG && (U + 1) % SPS == 0)  // step t+1 opens a new stage
-        boundary(std::integral_constant<int, (U + 1) / SPS>{}, t0);
-      tsp_bf16x8 pf[RB][2];
-      qk(U + 1, sn);     // matrix pipe: next step's scores
-      softmax(sc, pf, false);  // vector pipe: this step's weights
-      pv(U, pf);         // matrix pipe: this step's output
-      if constexpr (LAG && (U + 2) % SPS == 0)  // the next stage's barrier, one phase early
-        boundary(std::integral_constant<int, (U + 2) / SPS>{}, t0);
-      rowmax(sn, mx);    // vector pipe: next step's row max
-    };
-    auto fast_group = [&]<int... Us>(std::integer_sequence<int, Us...>, auto lag_const, int t0) {
-      (fast_step(std::integral_constant<int, Us>{}, lag_const, t0), ...);
-    };
-    int t = 0;
-    constexpr bool PINGPONG = TSP_PINGPONG && SPS == 2 && NW % 2 == 0;
-    if (PINGPONG && TSP_PP_LAGGED(wave)) {
-      for (; t + GROUP <= t_fast; t += GROUP) {
-        if constexpr (NR == 3) ring_poll_upto(t / SPS + PD + GROUP / SPS);  // the stages this group loads
-        fast_group(std::make_integer_sequence<int, GROUP>{}, std::bool_constant<PINGPONG>{}, t);
-      }
-    } else {
-      for (; t + GROUP <= t_fast; t += GROUP) {
-        if constexpr (NR == 3) ring_poll_upto(t / SPS + PD + GROUP / SPS);
-        fast_group(std::make_integer_sequence<int, GROUP>{}, std::false_type{}, t);
-      }
-    }
-    int issued = t > 0 ? t / SPS + PD : pro;  // last stage issued so far
-
-    // General path: the masked steps near the diagonal, the partial last stage and the
-    // ring drain.
-    for (; t < n_kv; ++t) {
-      if (rescale_needed(mx)) rescale(mx);
-      tsp_bf16x8 pf[RB][2];
-      if (t + 1 < n_kv) {
-        if ((t + 1) % SPS == 0) {
-          stage_ready((t + 1) / SPS, issued);
-          if (issued + 1 < n_stage) issue_stage(++issued);
+      const int t_fast = u_left == 0 && attempt == 0 ? min(t_unmasked - 1, (n_full - PD) * SPS - 1) : 0;
+      tsp_f32x16 s_alt[RB];
+      // Stage boundary: wait until stage NEXT (relative to t0 / SPS) landed for every wave,
+      // then issue the stage PD ahead into the slot two stages back.
+      auto boundary = [&](auto next_const, int t0) {
+        constexpr int NEXT = decltype(next_const)::value;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // that stage landed (this wave's part)
+        __syncthreads();  // ... for every wave; the slot two stages back is free again
+        const int32_t sg = t0 / SPS + NEXT + PD;  // the stage to issue
+        int64_t adv = (int64_t)sg * stage_stride;
+        if constexpr (NR == 3) adv = (int64_t)ring_stage_key(sg) * kv_row_stride;
+        const uint16_t* kb = kbase;
+        const uint16_t* vb = vbase;
+        if constexpr (NR == 2) {
+          if (sg >= n_stage1) {  // a stage of the second range
+            kb = kbase2;
+            vb = vbase2;
+            adv -= stage_off2;
+          }
         }
-        qk(t + 1, s_alt);
-        softmax(s_cur, pf, true);
-        pv(t, pf);
-        if (needs_mask(t + 1)) mask(t + 1, s_alt);
-        rowmax(s_alt, mx);
+        const uint32_t base = smem_addr + ((NEXT + PD) % NBUF) * St::SLOT_STRIDE;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_alt[rb];
+        for (int q = 0; q < St::LPW; ++q)
+          tsp_lds_dma16((dma_isv[q] ? vb : kb) + adv, dma_voff[q], base + dma_slot[q]);
+      };
+      // LAG (second half of the waves, one of the two waves of each SIMD): the barrier of
+      // stage k comes after the PV products of step SPS*k - 2 instead of before the QK
+      // products of step SPS*k - 1. Every barrier still precedes the first read of its stage
+      // and follows the last read of the stage two back, but the two waves of a SIMD then run
+      // their matrix and vector phases in alternation (one's softmax under the other's MFMAs).
+      auto fast_step = [&](auto u_const, auto lag_const, int t0) {
+        constexpr int U = decltype(u_const)::value;  // step t = t0 + U, t0 a multiple of GROUP
+        constexpr bool LAG = decltype(lag_const)::value;
+        tsp_f32x16(&sc)[RB] = (U % 2 == 0) ? s_cur : s_alt;
+        tsp_f32x16(&sn)[RB] = (U % 2 == 0) ? s_alt : s_cur;
+        if constexpr (!FIXED_MAX) {
+          if (rescale_needed(mx)) rescale(mx);
+        }
+        if constexpr (!LAG && (U + 1) % SPS == 0)  // step t+1 opens a new stage
+          boundary(std::integral_constant<int, (U + 1) / SPS>{}, t0);
+        tsp_bf16x8 pf[RB][2];
+        qk(U + 1, sn);     // matrix pipe: next step's scores
+        softmax(sc, pf, false);  // vector pipe: this step's weights
+        pv(U, pf);         // matrix pipe: this step's output
+        if constexpr (LAG && (U + 2) % SPS == 0)  // the next stage's barrier, one phase early
+          boundary(std::integral_constant<int, (U + 2) / SPS>{}, t0);
+        if constexpr (!FIXED_MAX) rowmax(sn, mx);  // vector pipe: next step's row max
+      };
+      auto fast_group = [&]<int... Us>(std::integer_sequence<int, Us...>, auto lag_const, int t0) {
+        (fast_step(std::integral_constant<int, Us>{}, lag_const, t0), ...);
+      };
+      // PINNED (one wave per SIMD, one step per stage, one row block): each step in a fixed
+      // issue order, since no second wave covers this wave's waits. Phase A: the QK^T
+      // products of step t+1, each with the K read KW products ahead of it, one V^T operand
+      // of step t read and one weight of step t computed. Phase B: the 16 PV products of
+      // step t back to back; after the 4th, the stage boundary (stage t+2 landed, barrier),
+      // then the first KW K operands of step t+2 and the load of stage t+4 into the slot of
+      // stage t, whose reads all ended before the barrier.
+      constexpr bool PINNED = FIXED_MAX && SPS == 1 && RB == 1 && TSP_FWD_PINNED;
+      constexpr int KW = 4;
+      static_assert(!PINNED || (KW + St::LPW <= 12 && NBUF == 4), "phase B holds the reads and loads");
+      tsp_bf16x8 kw[KW];  // the first K operands of the next step's QK^T products
+      auto kread = [&](const uint8_t* kt, int kk) {
+        return __builtin_bit_cast(tsp_bf16x8,
+                                  *reinterpret_cast<const tsp_u32x4*>(kt + koff[kk % KP] + (kk / KP) * St::SWZ * 16));
+      };
+      auto vread = [&](const uint8_t* vt, int j) {  // PV operand j: st = j / NDB, db = j % NDB
+        const uint8_t* a = vt + voff[(j % NDB) % VP] + ((j % NDB) / VP) * St::SWZ * 16 + (j / NDB) * 16 * St::ROW_BYTES;
+        const tsp_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a));
+        const tsp_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(a + 8 * St::ROW_BYTES));
+        return tsp_bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      auto pinned_step = [&](auto u_const, int t0) {
+        constexpr int U = decltype(u_const)::value;  // step t = t0 + U, t0 a multiple of NBUF
+        tsp_f32x16& sc = (U % 2 == 0) ? s_cur[0] : s_alt[0];
+        tsp_f32x16& sn = (U % 2 == 0) ? s_alt[0] : s_cur[0];
+        const uint8_t* kt = smem + ((U + 1) % NBUF) * St::SLOT_STRIDE;  // K of step t+1
+        const uint8_t* vt = smem + (U % NBUF) * St::SLOT_STRIDE;        // V of step t
+        const uint8_t* kt2 = smem + ((U + 2) % NBUF) * St::SLOT_STRIDE;  // K of step t+2
+        tsp_bf16x8 kf[NKK], vf[2 * NDB];
+        float pw[16];
+        tsp_u32x4 w[2];
+        float lsum = 0.f;
+        const float mneg = -m_run[0];
+#pragma unroll
+        for (int j = 0; j < KW; ++j) kf[j] = kw[j];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sn[e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {  // phase A
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[0][j], sn, 0, 0, 0);
+          if (j + KW < NKK) kf[j + KW] = kread(kt, j + KW);
+          vf[j] = vread(vt, j);
+          pw[j] = tsp_exp2(fmaf(sc[j], p.scale_log2, mneg));
+          if (j & 1) {
+            w[j / 8][(j % 8) / 2] = tsp_pack_bf16(pw[j - 1], pw[j]);
+            lsum = tsp_sum_bf16_pair(w[j / 8][(j % 8) / 2], lsum);  // the rounded weights, as PV applies them
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run[0] += lsum;
+        const tsp_bf16x8 pf0 = __builtin_bit_cast(tsp_bf16x8, w[0]), pf1 = __builtin_bit_cast(tsp_bf16x8, w[1]);
+        // the load of stage t+4 (a stage of the second range past the first's stages)
+        const int32_t sg = t0 + U + 4;
+        int64_t adv = (int64_t)sg * stage_stride;
+        const uint16_t* kb = kbase;
+        const uint16_t* vb = vbase;
+        if constexpr (NR == 2) {
+          if (sg >= n_stage1) {
+            kb = kbase2;
+            vb = vbase2;
+            adv -= stage_off2;
+          }
+        }
+        const uint32_t base = smem_addr + ((U + 4) % NBUF) * St::SLOT_STRIDE;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {  // phase B
+          acc[0][j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], j < NDB ? pf0 : pf1, acc[0][j % NDB], 0, 0, 0);
+          if (j == 3) {
+            __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // stage t+2 landed (this wave's part)
+            __syncthreads();  // ... for every wave; every read of stage t is done
+          }
+          if (j >= 4 && j < 4 + KW) kw[j - 4] = kread(kt2, j - 4);
+          if (j >= 4 + KW && j < 4 + KW + St::LPW) {
+            const int q = j - 4 - KW;
+            tsp_lds_dma16((dma_isv[q] ? vb : kb) + adv, dma_voff[q], base + dma_slot[q]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      auto pinned_group = [&]<int... Us>(std::integer_sequence<int, Us...>, int t0) {
+        (pinned_step(std::integral_constant<int, Us>{}, t0), ...);
+      };
+      int t = 0;
+      constexpr bool PINGPONG = TSP_PINGPONG && SPS == 2 && NW % 2 == 0;
+      if constexpr (PINNED) {
+        // one stage less ahead: the last pinned step loads stage t+4
+        const int t_pin = min(t_fast, (n_full - PD - 1) * SPS - 1);
+        if (t_pin >= GROUP) {
+          boundary(std::integral_constant<int, 1>{}, 0);  // stage 1 ready; stage 3 issued
+#pragma unroll
+          for (int j = 0; j < KW; ++j) kw[j] = kread(smem + 1 * St::SLOT_STRIDE, j);
+          for (; t + GROUP <= t_pin; t += GROUP) pinned_group(std::make_integer_sequence<int, GROUP>{}, t);
+        }
+      } else if (PINGPONG && TSP_PP_LAGGED(wave)) {
+        for (; t + GROUP <= t_fast; t += GROUP) {
+          if constexpr (NR == 3) ring_poll_upto(t / SPS + PD + GROUP / SPS);  // the stages this group loads
+          fast_group(std::make_integer_sequence<int, GROUP>{}, std::bool_constant<PINGPONG>{}, t);
+        }
       } else {
-        softmax(s_cur, pf, true);
-        pv(t, pf);
+        for (; t + GROUP <= t_fast; t += GROUP) {
+          if constexpr (NR == 3) ring_poll_upto(t / SPS + PD + GROUP / SPS);
+          fast_group(std::make_integer_sequence<int, GROUP>{}, std::false_type{}, t);
+        }
       }
-    }
+      if constexpr (FIXED_MAX) {
+        if (t > 0) rowmax(s_cur, mx);  // the next step's scores (GROUP is even)
+      }
+      int issued = t > 0 ? t / SPS + PD + (PINNED ? 1 : 0) : pro;  // last stage issued so far
+      // PINNED: the last stage already waited for (and barriered) by the pinned steps. Every
+      // wave takes barrier k when stage k+1 is ready and then loads stage k+3, on either path.
+      const int ready = PINNED && t > 0 ? t + 1 : 0;
+
+      // General path: the masked steps near the diagonal, the partial last stage and the
+      // ring drain.
+      for (; t < n_kv; ++t) {
+        if (rescale_needed(mx)) rescale(mx);
+        tsp_bf16x8 pf[RB][2];
+        if (t + 1 < n_kv) {
+          if ((t + 1) % SPS == 0 && (!PINNED || (t + 1) / SPS > ready)) {
+            stage_ready((t + 1) / SPS, issued);
+            if (issued + 1 < n_stage) issue_stage(++issued);
+          }
+          qk(t + 1, s_alt);
+          softmax(s_cur, pf, true);
+          pv(t, pf);
+          if (needs_mask(t + 1)) mask(t + 1, s_alt);
+          rowmax(s_alt, mx);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_alt[rb];
+        } else {
+          softmax(s_cur, pf, true);
+          pv(t, pf);
+        }
+      }
+      if constexpr (!FIXED_MAX) break;
+      if (attempt > 0) break;
+      // an infinite or NaN sum or output (exponent field all ones) anywhere in the workgroup
+      uint32_t top = 0;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        top = max(top, __float_as_uint(l_run[rb]) & 0x7fffffffu);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) top = max(top, __float_as_uint(acc[rb][db][e]) & 0x7fffffffu);
+      }
+      if (!__syncthreads_or(top >= 0x7f800000u)) break;
+    }  // attempt
 
     // ---- epilogue: normalise, round to bf16, write O and lse -----------------------------
     if (p.accumulate) {  // merge this partial into the running result (out, lse)

@@ -271,6 +271,42 @@ def test_large_masked_scores_do_not_leak():
     check(out, lse, ref_out, ref_lse, torch.bfloat16, C=S // (2 * D))
 
 
+def _rising_scores(growth, seed, S=8192, D=2, r=0):
+    """A dh-256 shard whose scores rise along the key index: q_i[0] = 8 and k_j[0] =
+    growth * j / S, the other dims N(0, 1). Returns the inputs and, for the row at the
+    largest position, its highest score minus its highest score over the first 32 keys,
+    in log2 units (how far above a running max taken at the first step the weights go)."""
+    q, k, v = workloads.make_custom(1, S, D, 2, 1, 256, torch.bfloat16, seed=seed)
+    q[..., 0] = 8.0
+    k[0, :, 0, 0] = (torch.arange(S, dtype=torch.float64) * growth / S).to(torch.bfloat16)
+    pos = oracle.zigzag_positions(S, D, r)
+    i = int(np.argmax(pos))
+    s = k[0, : pos[i] + 1, 0].double().numpy() @ q[0, i].double().numpy().T / 16.0  # [keys, heads]
+    rise = float((s.max(axis=0) - s[:32].max(axis=0)).max() / math.log(2))
+    return q, k, v, rise
+
+
+def test_dh256_scores_far_above_the_first_step():
+    """The dh-256 kernel's unrolled steps keep the running max of their first step; weights
+    up to 2^(rise) stay finite and the result must match the oracle."""
+    q, k, v, rise = _rising_scores(growth=100.0, seed=41)
+    assert 40.0 < rise < 100.0, rise
+    out, lse = run(q, k, v, 2, 0)
+    ref_out, ref_lse = oracle.causal_attention(q, k, v, 2, 0)
+    check(out, lse, ref_out, ref_lse, torch.bfloat16, C=8192 // 4)
+
+
+def test_dh256_overflow_is_swept_again():
+    """Scores rising far past the fp32 range of 2^(score - first-step max) overflow the
+    fixed-max sweep; the tile must be swept again with the running max tested every step
+    and still match the oracle."""
+    q, k, v, rise = _rising_scores(growth=400.0, seed=43)
+    assert rise > 160.0, rise
+    out, lse = run(q, k, v, 2, 0)
+    ref_out, ref_lse = oracle.causal_attention(q, k, v, 2, 0)
+    check(out, lse, ref_out, ref_lse, torch.bfloat16, C=8192 // 4)
+
+
 # -- structural identities ---------------------------------------------------------------
 
 def test_concatenation_of_all_ranks_equals_unsharded():
