@@ -34,10 +34,11 @@
 //    reach past a wave's first position apply the element mask (key > position -> -inf).
 //  * Online softmax in base 2 (log2(e)/sqrt(dh) folded into one FMA), running max raised
 //    lazily (TSP_RESCALE_SLACK), row sums from the rounded bf16 weights (v_dot2).
-//  * dh 256 runs one wave per SIMD (its Q^T operands and output fill the registers), so
-//    no second wave covers a wave's own waits. Its unrolled steps keep the running max of
+//  * dh 256 (and dh 128 with two row blocks per wave, which halves the LDS reads per
+//    product) runs one wave per SIMD: its Q^T operands and outputs fill the registers, and
+//    no second wave covers a wave's own waits. The unrolled steps keep the running max of
 //    the sweep's first step (no per-step test and branch; a tile that overflowed is swept
-//    again with the test) and are issued in a fixed order: K operands read four products
+//    again with the test) and are issued in a fixed order: K operands read four operands
 //    ahead, the V^T operands and the weights of step t under the QK^T products of step
 //    t+1, then the PV products back to back with the stage boundary and the next loads
 //    under them.
@@ -161,6 +162,15 @@ struct Bf16Stage {
 #ifndef TSP_FWD_PINNED
 #define TSP_FWD_PINNED 1
 #endif
+#ifndef TSP_PIN_KW
+#define TSP_PIN_KW 0  // 0: 4 K operands ahead with one row block, 2 with two
+#endif
+#ifndef TSP_PIN_BJ
+#define TSP_PIN_BJ 3
+#endif
+#ifndef TSP_PIN_SPLIT
+#define TSP_PIN_SPLIT 1
+#endif
 template <int DH, int NW, int RB, int NBUF, int SPS, int OCC, int NR>
 __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p) {
   using St = Bf16Stage<DH, NW, NBUF, SPS>;
@@ -168,12 +178,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
   constexpr int NDB = DH / 32;  // 32-dim blocks of the output
   constexpr int NKK = DH / 16;  // reduction steps of QK^T
   constexpr int PD = St::PD;
-  // dh 256 (one wave per SIMD, where the per-step test costs most): the unrolled steps keep
-  // the running max of their first step instead of testing every step's scores against it.
+  // One wave per SIMD with 256 output dims per row block pair or more (dh 256, or dh 128 with
+  // two row blocks), where the per-step test costs most: the unrolled steps keep the
+  // running max of the sweep's first step instead of testing every step's scores against it.
   // Their weights are then 2^(x - m) with m at most the row's true max, exact up to overflow;
   // a tile whose sums or outputs left the finite range is swept again with the test on
   // every step.
-  constexpr bool FIXED_MAX = DH == 256 && NR != 3 && TSP_FWD_FIXED_MAX;
+  constexpr bool FIXED_MAX = OCC == 1 && RB * DH >= 256 && NR != 3 && TSP_FWD_FIXED_MAX;
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * St::STAGE_BYTES];
 
@@ -709,17 +720,35 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       auto fast_group = [&]<int... Us>(std::integer_sequence<int, Us...>, auto lag_const, int t0) {
         (fast_step(std::integral_constant<int, Us>{}, lag_const, t0), ...);
       };
-      // PINNED (one wave per SIMD, one step per stage, one row block): each step in a fixed
-      // issue order, since no second wave covers this wave's waits. Phase A: the QK^T
-      // products of step t+1, each with the K read KW products ahead of it, one V^T operand
-      // of step t read and one weight of step t computed. Phase B: the 16 PV products of
-      // step t back to back; after the 4th, the stage boundary (stage t+2 landed, barrier),
-      // then the first KW K operands of step t+2 and the load of stage t+4 into the slot of
-      // stage t, whose reads all ended before the barrier.
-      constexpr bool PINNED = FIXED_MAX && SPS == 1 && RB == 1 && TSP_FWD_PINNED;
-      constexpr int KW = 4;
-      static_assert(!PINNED || (KW + St::LPW <= 12 && NBUF == 4), "phase B holds the reads and loads");
+      // PINNED (one wave per SIMD, one step per stage): each step in a fixed issue order,
+      // since no second wave covers this wave's waits. Phase A: the 16 QK^T products of step
+      // t+1, each K operand read KW operands ahead of its products, and under each product
+      // an equal share of the V^T operand reads and of the weights of step t. Phase B: the
+      // 16 PV products of step t back to back; after product BJ, the stage boundary (stage
+      // t+2 landed, barrier), then the first KW K operands of step t+2 and the load of stage
+      // t+4 into the slot of stage t, whose reads all ended before the barrier.
+      constexpr bool PINNED = FIXED_MAX && SPS == 1 && TSP_FWD_PINNED;
+      constexpr int KW = TSP_PIN_KW > 0 ? TSP_PIN_KW : RB == 1 ? 4 : 2, BJ = TSP_PIN_BJ;
+      constexpr int NOPS = KW + St::LPW, PER = (NOPS + 14 - BJ) / (15 - BJ);  // ops per PV product after the barrier
+      static_assert(!PINNED || (NBUF == 4 && NKK * RB == 16 && 2 * NDB * RB == 16), "16 + 16 products a step, 4 slots");
       tsp_bf16x8 kw[KW];  // the first K operands of the next step's QK^T products
+      // SPLIT (two row blocks): row block 0's weights of step t+1 are computed under the PV
+      // products of step t, so each product of both phases carries one weight
+      constexpr bool SPLIT = PINNED && RB == 2 && TSP_PIN_SPLIT;
+      tsp_u32x4 wc[2];  // SPLIT: row block 0's rounded weights of the next step
+      float lc = 0.f;   // ... and their sum
+      // weight e (0..15) of a row: 2^(score * scale - m), rounded to bf16 in pairs; the row
+      // sum takes the rounded pairs, as PV applies them
+      auto weight = [&](float score, float mn, float(&pwr)[16], tsp_u32x4(&wr)[2], float& ls, int e,
+                        bool here = false) {
+        pwr[e] = tsp_exp2(fmaf(score, p.scale_log2, mn));
+        if (here) asm volatile("" : "+v"(pwr[e]));  // computed at this point of the order, not where used
+        if (e & 1) {
+          wr[e / 8][(e % 8) / 2] = tsp_pack_bf16(pwr[e - 1], pwr[e]);
+          ls = tsp_sum_bf16_pair(wr[e / 8][(e % 8) / 2], ls);
+          if (here) asm volatile("" : "+v"(ls));
+        }
+      };
       auto kread = [&](const uint8_t* kt, int kk) {
         return __builtin_bit_cast(tsp_bf16x8,
                                   *reinterpret_cast<const tsp_u32x4*>(kt + koff[kk % KP] + (kk / KP) * St::SWZ * 16));
@@ -732,34 +761,48 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
       };
       auto pinned_step = [&](auto u_const, int t0) {
         constexpr int U = decltype(u_const)::value;  // step t = t0 + U, t0 a multiple of NBUF
-        tsp_f32x16& sc = (U % 2 == 0) ? s_cur[0] : s_alt[0];
-        tsp_f32x16& sn = (U % 2 == 0) ? s_alt[0] : s_cur[0];
+        constexpr int NV = 2 * NDB;                   // V^T operands of a step
+        tsp_f32x16(&sc)[RB] = (U % 2 == 0) ? s_cur : s_alt;
+        tsp_f32x16(&sn)[RB] = (U % 2 == 0) ? s_alt : s_cur;
         const uint8_t* kt = smem + ((U + 1) % NBUF) * St::SLOT_STRIDE;  // K of step t+1
         const uint8_t* vt = smem + (U % NBUF) * St::SLOT_STRIDE;        // V of step t
         const uint8_t* kt2 = smem + ((U + 2) % NBUF) * St::SLOT_STRIDE;  // K of step t+2
-        tsp_bf16x8 kf[NKK], vf[2 * NDB];
-        float pw[16];
-        tsp_u32x4 w[2];
-        float lsum = 0.f;
-        const float mneg = -m_run[0];
+        tsp_bf16x8 kf[NKK], vf[NV];
+        float pw[RB][16], lsum[RB], mneg[RB];
+        tsp_u32x4 w[RB][2];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          lsum[rb] = 0.f;
+          mneg[rb] = -m_run[rb];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sn[rb][e] = 0.f;
+        }
 #pragma unroll
         for (int j = 0; j < KW; ++j) kf[j] = kw[j];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sn[e] = 0.f;
+        for (int j = 0; j < 16; ++j) {  // phase A: product j is (K operand j / RB, row block j % RB)
+          const int kk = j / RB, rq = j % RB;
+          sn[rq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[rq][kk], sn[rq], 0, 0, 0);
+          if (rq == 0 && kk + KW < NKK) kf[kk + KW] = kread(kt, kk + KW);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {  // phase A
-          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[0][j], sn, 0, 0, 0);
-          if (j + KW < NKK) kf[j + KW] = kread(kt, j + KW);
-          vf[j] = vread(vt, j);
-          pw[j] = tsp_exp2(fmaf(sc[j], p.scale_log2, mneg));
-          if (j & 1) {
-            w[j / 8][(j % 8) / 2] = tsp_pack_bf16(pw[j - 1], pw[j]);
-            lsum = tsp_sum_bf16_pair(w[j / 8][(j % 8) / 2], lsum);  // the rounded weights, as PV applies them
+          for (int o = j * NV / 16; o < (j + 1) * NV / 16; ++o) vf[o] = vread(vt, o);
+          if constexpr (SPLIT) {
+            weight(sc[1][j], mneg[1], pw[1], w[1], lsum[1], j);
+          } else {
+#pragma unroll
+            for (int x = j * RB; x < (j + 1) * RB; ++x)  // weight x: row block x / 16, score x % 16
+              weight(sc[x / 16][x % 16], mneg[x / 16], pw[x / 16], w[x / 16], lsum[x / 16], x % 16);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        l_run[0] += lsum;
-        const tsp_bf16x8 pf0 = __builtin_bit_cast(tsp_bf16x8, w[0]), pf1 = __builtin_bit_cast(tsp_bf16x8, w[1]);
+        tsp_bf16x8 pf[RB][2];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const bool carried = SPLIT && rb == 0;
+          l_run[rb] += carried ? lc : lsum[rb];
+          pf[rb][0] = __builtin_bit_cast(tsp_bf16x8, carried ? wc[0] : w[rb][0]);
+          pf[rb][1] = __builtin_bit_cast(tsp_bf16x8, carried ? wc[1] : w[rb][1]);
+        }
         // the load of stage t+4 (a stage of the second range past the first's stages)
         const int32_t sg = t0 + U + 4;
         int64_t adv = (int64_t)sg * stage_stride;
@@ -774,18 +817,32 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
         }
         const uint32_t base = smem_addr + ((U + 4) % NBUF) * St::SLOT_STRIDE;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {  // phase B
-          acc[0][j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], j < NDB ? pf0 : pf1, acc[0][j % NDB], 0, 0, 0);
-          if (j == 3) {
+        for (int j = 0; j < 16; ++j) {  // phase B: product j is (V^T operand j / RB, row block j % RB)
+          const int o = j / RB, rq = j % RB;
+          acc[rq][o % NDB] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[o], pf[rq][o / NDB], acc[rq][o % NDB], 0, 0, 0);
+          if (j == BJ) {
             __builtin_amdgcn_s_waitcnt(0x0F70 | VM_STEADY);  // stage t+2 landed (this wave's part)
             __syncthreads();  // ... for every wave; every read of stage t is done
           }
-          if (j >= 4 && j < 4 + KW) kw[j - 4] = kread(kt2, j - 4);
-          if (j >= 4 + KW && j < 4 + KW + St::LPW) {
-            const int q = j - 4 - KW;
-            tsp_lds_dma16((dma_isv[q] ? vb : kb) + adv, dma_voff[q], base + dma_slot[q]);
+          if (j > BJ) {
+#pragma unroll
+            for (int o = (j - BJ - 1) * PER; o < (j - BJ) * PER && o < NOPS; ++o) {
+              if (o < KW) {
+                kw[o] = kread(kt2, o);
+              } else {
+                const int q = o - KW;
+                tsp_lds_dma16((dma_isv[q] ? vb : kb) + adv, dma_voff[q], base + dma_slot[q]);
+              }
+            }
           }
+          if constexpr (SPLIT) weight(sn[0][j], mneg[0], pw[0], w[0], lsum[0], j, true);  // step t+1
           __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (SPLIT) {
+          wc[0] = w[0][0];
+          wc[1] = w[0][1];
+          lc = lsum[0];
         }
       };
       auto pinned_group = [&]<int... Us>(std::integer_sequence<int, Us...>, int t0) {
@@ -800,6 +857,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_fwd_bf16_kernel(TspParams p
           boundary(std::integral_constant<int, 1>{}, 0);  // stage 1 ready; stage 3 issued
 #pragma unroll
           for (int j = 0; j < KW; ++j) kw[j] = kread(smem + 1 * St::SLOT_STRIDE, j);
+          if constexpr (SPLIT) {  // row block 0's weights of the first pinned step
+            float pw0[16];
+            lc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) weight(s_cur[0][e], -m_run[0], pw0, wc, lc, e);
+          }
           for (; t + GROUP <= t_pin; t += GROUP) pinned_group(std::make_integer_sequence<int, GROUP>{}, t);
         }
       } else if (PINGPONG && TSP_PP_LAGGED(wave)) {

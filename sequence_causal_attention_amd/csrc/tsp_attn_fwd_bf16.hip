@@ -12,48 +12,65 @@ namespace {
 
 using tsp_host::KernelShape;
 
-// Tile configuration of the bf16 kernels per head dim: waves per workgroup, 32-row query
-// blocks per wave, depth of the LDS stage ring, target waves per SIMD.
+// Tile configuration of the bf16 kernels per head dim and launch form (NR: 1 one key range,
+// 2 two ranges, 3 the ring sweep): waves per workgroup, 32-row query blocks per wave, depth
+// of the LDS stage ring, 32-key steps per stage, target waves per SIMD.
+// dh 128: one-range launches run one wave per SIMD with two row blocks each (the fixed-max
+// sweep in a pinned issue order, at half the LDS reads per product); two-range and ring
+// launches, whose sweeps are short and whose masked diagonal steps weigh more, keep two
+// waves per SIMD with one row block. Both have 8 row blocks per workgroup, so the host's
+// tile plan (kernel shape) is the same for every form.
 #ifndef TSP_DH128_NW
-#define TSP_DH128_NW 8
+#define TSP_DH128_NW 4
 #endif
 #ifndef TSP_DH128_NBUF
-#define TSP_DH128_NBUF 5
+#define TSP_DH128_NBUF 4
 #endif
 #ifndef TSP_DH128_SPS
-#define TSP_DH128_SPS 2
+#define TSP_DH128_SPS 1
 #endif
 #ifndef TSP_DH128_RB
-#define TSP_DH128_RB 1
+#define TSP_DH128_RB 2
 #endif
 #ifndef TSP_DH128_OCC
-#define TSP_DH128_OCC 2
+#define TSP_DH128_OCC 1
 #endif
-template <int DH>
+struct CfgWave2 {  // dh 128, two waves per SIMD
+  static constexpr int NW = 8, RB = 1, NBUF = 5, SPS = 2, OCC = 2;
+};
+template <int DH, int NR>
 struct Bf16Cfg;
-template <>
-struct Bf16Cfg<64> {
+template <int NR>
+struct Bf16Cfg<64, NR> {
   static constexpr int NW = 4, RB = 2, NBUF = 4, SPS = 1, OCC = 1;
 };
 template <>
-struct Bf16Cfg<128> {
+struct Bf16Cfg<128, 1> {
   static constexpr int NW = TSP_DH128_NW, RB = TSP_DH128_RB, NBUF = TSP_DH128_NBUF, SPS = TSP_DH128_SPS,
                        OCC = TSP_DH128_OCC;
 };
 template <>
-struct Bf16Cfg<256> {
+struct Bf16Cfg<128, 2> : CfgWave2 {};
+template <>
+struct Bf16Cfg<128, 3> : CfgWave2 {};
+template <int NR>
+struct Bf16Cfg<256, NR> {
   static constexpr int NW = 4, RB = 1, NBUF = 4, SPS = 1, OCC = 1;
 };
 
 template <int DH>
 KernelShape shape_of() {
-  using C = Bf16Cfg<DH>;
+  using C = Bf16Cfg<DH, 1>;
+  static_assert(C::NW * C::RB == Bf16Cfg<DH, 2>::NW * Bf16Cfg<DH, 2>::RB &&
+                    C::NW * C::RB == Bf16Cfg<DH, 3>::NW * Bf16Cfg<DH, 3>::RB,
+                "every launch form has the same row blocks per workgroup");
+  static_assert(tsp::Bf16Stage<DH, C::NW, C::NBUF, C::SPS>::BK == 32, "32-key steps");
   return KernelShape{tsp::Bf16Stage<DH, C::NW, C::NBUF, C::SPS>::BK, C::NW, C::RB};
 }
 
 template <int DH, int NR>
 void launch(const TspParams& p, hipStream_t stream) {
-  using C = Bf16Cfg<DH>;
+  using C = Bf16Cfg<DH, NR>;
   hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::SPS, C::OCC, NR>), dim3(p.n_units),
                      dim3(C::NW * 64), 0, stream, p);
 }
