@@ -271,40 +271,60 @@ def test_large_masked_scores_do_not_leak():
     check(out, lse, ref_out, ref_lse, torch.bfloat16, C=S // (2 * D))
 
 
-def _rising_scores(growth, seed, S=8192, D=2, r=0):
-    """A dh-256 shard whose scores rise along the key index: q_i[0] = 8 and k_j[0] =
-    growth * j / S, the other dims N(0, 1). Returns the inputs and, for the row at the
-    largest position, its highest score minus its highest score over the first 32 keys,
-    in log2 units (how far above a running max taken at the first step the weights go)."""
-    q, k, v = workloads.make_custom(1, S, D, 2, 1, 256, torch.bfloat16, seed=seed)
+def _rising_scores(rise_target, seed, dh, S=8192, D=2, r=0):
+    """A shard whose scores rise along the key index: q_i[0] = 8 and k_j[0] = g * j / S with
+    g chosen so that the last row's top score lies about `rise_target` log2 units above its
+    top score over the first 32 keys; the other dims N(0, 1). Returns the inputs and that
+    rise as it comes out of the rounded inputs (how far above a running max taken at the
+    sweep's first step the weights go)."""
+    q, k, v = workloads.make_custom(1, S, D, 2, 1, dh, torch.bfloat16, seed=seed)
+    growth = rise_target * math.sqrt(dh) * math.log(2) / 8.0
     q[..., 0] = 8.0
     k[0, :, 0, 0] = (torch.arange(S, dtype=torch.float64) * growth / S).to(torch.bfloat16)
     pos = oracle.zigzag_positions(S, D, r)
     i = int(np.argmax(pos))
-    s = k[0, : pos[i] + 1, 0].double().numpy() @ q[0, i].double().numpy().T / 16.0  # [keys, heads]
+    s = k[0, : pos[i] + 1, 0].double().numpy() @ q[0, i].double().numpy().T / math.sqrt(dh)  # [keys, heads]
     rise = float((s.max(axis=0) - s[:32].max(axis=0)).max() / math.log(2))
     return q, k, v, rise
 
 
-def test_dh256_scores_far_above_the_first_step():
-    """The dh-256 kernel's unrolled steps keep the running max of their first step; weights
-    up to 2^(rise) stay finite and the result must match the oracle."""
-    q, k, v, rise = _rising_scores(growth=100.0, seed=41)
+# The kernels that run one wave per SIMD (dh 256; dh 128 one-range launches) keep the running
+# max of the sweep's first step in their unrolled steps: weights up to 2^rise must stay exact,
+# and an overflow must send the tile through a second, checked sweep.
+@pytest.mark.parametrize("dh", [128, 256])
+def test_scores_far_above_the_first_step(dh):
+    q, k, v, rise = _rising_scores(75.0, seed=41 + dh, dh=dh)
     assert 40.0 < rise < 100.0, rise
     out, lse = run(q, k, v, 2, 0)
     ref_out, ref_lse = oracle.causal_attention(q, k, v, 2, 0)
     check(out, lse, ref_out, ref_lse, torch.bfloat16, C=8192 // 4)
 
 
-def test_dh256_overflow_is_swept_again():
-    """Scores rising far past the fp32 range of 2^(score - first-step max) overflow the
-    fixed-max sweep; the tile must be swept again with the running max tested every step
-    and still match the oracle."""
-    q, k, v, rise = _rising_scores(growth=400.0, seed=43)
+@pytest.mark.parametrize("dh", [128, 256])
+def test_overflow_is_swept_again(dh):
+    q, k, v, rise = _rising_scores(290.0, seed=43 + dh, dh=dh)
     assert rise > 160.0, rise
     out, lse = run(q, k, v, 2, 0)
     ref_out, ref_lse = oracle.causal_attention(q, k, v, 2, 0)
     check(out, lse, ref_out, ref_lse, torch.bfloat16, C=8192 // 4)
+
+
+def test_overflow_in_a_two_range_launch():
+    """The dh-256 two-range launch (the rank's two own chunks, one sweep over both) with
+    scores rising past the fp32 range of the fixed-max weights in the second range: the
+    result must equal the oracle's attention over the union of the two ranges."""
+    S, D, r = 8192, 2, 0
+    q, k, v, rise = _rising_scores(290.0, seed=47, dh=256, S=S, D=D, r=r)
+    assert rise > 160.0, rise
+    C = S // (2 * D)
+    ra, rb = (r * C, (r + 1) * C), ((2 * D - 1 - r) * C, (2 * D - r) * C)
+    o, l = tsp.fwd(q.to(DEV), k.to(DEV), v.to(DEV), D=D, rank=r, kv_range=ra, kv_range2=rb)
+    torch.cuda.synchronize()
+    out, lse = o.float().cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64)
+    oa, la = oracle.causal_attention_range(q, k, v, D, r, *ra)
+    ob, lb = oracle.causal_attention_range(q, k, v, D, r, *rb)
+    ref_out, ref_lse = oracle.merge_partials(oa, la, ob, lb)
+    check(out, lse, ref_out, ref_lse, torch.bfloat16, C=C)
 
 
 # -- structural identities ---------------------------------------------------------------
