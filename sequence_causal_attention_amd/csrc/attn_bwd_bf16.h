@@ -244,11 +244,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
   const int32_t n_steps = p.grp * tiles;  // step u: head hk*grp + u/tiles, tile t_first + u%tiles
 
   // ---- per-lane LDS offsets -------------------------------------------------------------
-  int qoff[NKK];  // row-wise A operand read: row `col`, chunk 2kk + half
+  // At dh 256 (its registers are short) one offset per 16-chunk swizzle period: the
+  // swizzle only changes the low 4 bits of the chunk index, so chunks 16 apart lie 256
+  // bytes apart and QP (TP) offsets serve all NKK (NDB) operands.
+  constexpr int QP = DH == 256 ? NKK / 2 : NKK, TP = DH == 256 ? NDB / 2 : NDB;
+  int qoff[QP];  // row-wise A operand read: row `col`, chunk 2kk + half
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
+  for (int kk = 0; kk < QP; ++kk)
     qoff[kk] = col * T::ROW_BYTES + (((2 * kk + half) ^ tsp_swz_rt<T::CPR>(col)) << 4);
-  int tlo[NDB], thi[NDB];  // transposing reads
+  auto qo = [&](int kk) __attribute__((always_inline)) { return qoff[kk % QP] + (kk / QP) * 256; };
+  int tlo[NDB], thi[NDB];  // transposing reads (the first TP are used)
   tsp_tr_offsets<DH>(lane, tlo, thi);
 
   // ---- this wave's share of a stage load --------------------------------------------------
@@ -331,13 +336,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
     }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const tsp_bf16x8 qa = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(qs + qoff[kk]));
+      const tsp_bf16x8 qa = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(qs + qo(kk)));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
     }
     if constexpr (DO_DK) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const tsp_bf16x8 da = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(ds + qoff[kk]));
+        const tsp_bf16x8 da = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(ds + qo(kk)));
         const tsp_bf16x8 vb =
             VLDS ? __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(vls + 1024 * kk)) : vf[kk];
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, dp, 0, 0, 0);
@@ -403,13 +408,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int ro = st * 16 * T::ROW_BYTES;
+        const int ro = st * 16 * T::ROW_BYTES + (db / TP) * 256;
         if constexpr (DO_DV) {
-          const tsp_bf16x8 doT = tsp_tr_read8(ds + tlo[db] + ro, ds + thi[db] + ro);
+          const tsp_bf16x8 doT = tsp_tr_read8(ds + tlo[db % TP] + ro, ds + thi[db % TP] + ro);
           dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doT, pf[st], dv[db], 0, 0, 0);
         }
         if constexpr (DO_DK) {
-          const tsp_bf16x8 qT = tsp_tr_read8(qs + tlo[db] + ro, qs + thi[db] + ro);
+          const tsp_bf16x8 qT = tsp_tr_read8(qs + tlo[db % TP] + ro, qs + thi[db % TP] + ro);
           dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf[st], dk[db], 0, 0, 0);
         }
       }
