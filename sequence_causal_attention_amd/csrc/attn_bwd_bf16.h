@@ -232,6 +232,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
       else if constexpr (DO_DK) vf[kk] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(vp + 16 * kk));
     }
   }
+  // Let these loads land here, once: otherwise the compiler waits for them (vmcnt) before
+  // their first use inside the step loop, on every step, and that count also covers the
+  // stage loads issued just before, so each step would wait for its own prefetch.
+  tsp_wait_vm<0>();
 
   // Query tiles to sweep: local rows are increasing in position, so the rows that see
   // key j0 are a suffix; it starts in the first chunk if j0 lies below that chunk's end.
@@ -321,7 +325,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
   // one per weight).
   const float meta_scale = half ? 1.0f : -TSP_LOG2E;
   auto prescale_meta = [&](const uint8_t* qs) __attribute__((always_inline)) {
-    float* m = reinterpret_cast<float*>(const_cast<uint8_t*>(qs) + 2 * T::TILE_BYTES + wave * T::META_BYTES) + lane;
+    // The lane's byte offset is formed here each time: a slot's metadata may lie past the
+    // 16-bit LDS offset field, and an address kept live per slot across the loop was spilled
+    // (its reload waits on vmcnt, which also drains the stage loads in flight).
+    uint32_t l4 = 4u * (uint32_t)lane;
+    asm volatile("" : "+v"(l4));
+    float* m = reinterpret_cast<float*>(const_cast<uint8_t*>(qs) + 2 * T::TILE_BYTES + wave * T::META_BYTES + l4);
     *m = *m * meta_scale;
   };
 
@@ -602,6 +611,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dq_bf16_kernel(TspBwdPa
     const int64_t li = ((int64_t)b * p.Hq + head) * p.S_local + lrow;
     const float lse2 = p.lse[li] * TSP_LOG2E;
     const float delta = bp.delta[li];
+    tsp_wait_vm<0>();  // these loads land here, not behind a wait in every step (see the dK/dV kernel)
 
     tsp_f32x16 acc[NDB];
 #pragma unroll
