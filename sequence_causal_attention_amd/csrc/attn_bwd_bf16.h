@@ -41,6 +41,9 @@
 #ifndef TSP_BWD_UNROLL_RING_NOPIPE
 #define TSP_BWD_UNROLL_RING_NOPIPE 1
 #endif
+#ifndef TSP_BWD_READ_AHEAD
+#define TSP_BWD_READ_AHEAD 1
+#endif
 
 namespace tsp {
 
@@ -252,6 +255,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
   // swizzle only changes the low 4 bits of the chunk index, so chunks 16 apart lie 256
   // bytes apart and QP (TP) offsets serve all NKK (NDB) operands.
   constexpr int QP = DH == 256 ? NKK / 2 : NKK, TP = DH == 256 ? NDB / 2 : NDB;
+  // RA (dh 256, one wave per SIMD): every LDS operand of the products read RAW products ahead
+  // of its product, in an order held by scheduling barriers. The compiler's own order read
+  // each one just before its product, so at one wave per SIMD every product waited the full
+  // LDS latency.
+  constexpr bool RA = DH == 256 && !VLDS && TSP_BWD_READ_AHEAD;
+  constexpr int RAW = 4;
   int qoff[QP];  // row-wise A operand read: row `col`, chunk 2kk + half
 #pragma unroll
   for (int kk = 0; kk < QP; ++kk)
@@ -343,6 +352,23 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
       s[e] = 0.f;
       dp[e] = 0.f;
     }
+    if constexpr (RA) {  // S then dP operands, each read RAW products ahead
+      constexpr int NP = DO_DK ? 2 * NKK : NKK;
+      tsp_bf16x8 ra[NP];
+      auto rd = [&](int j) __attribute__((always_inline)) {
+        return __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>((j < NKK ? qs : ds) + qo(j % NKK)));
+      };
+#pragma unroll
+      for (int j = 0; j < RAW; ++j) ra[j] = rd(j);
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        if (j + RAW < NP) ra[j + RAW] = rd(j + RAW);
+        if (j < NKK) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[j], kf[j], s, 0, 0, 0);
+        else dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[j], vf[j - NKK], dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const tsp_bf16x8 qa = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(qs + qo(kk)));
@@ -398,6 +424,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
       for (int v = 0; v < 16; ++v)
         if (8 * (v >> 2) + (v & 3) < lim) x[v] = -INFINITY;
     }
+    // RA: the transposed operands of the dV / dK products (dV then dK for each (st, db), the
+    // order below), the first RAW read ahead of the weights and each later one RAW products
+    // ahead of its product
+    constexpr int NT = (DO_DV ? 1 : 0) + (DO_DK ? 1 : 0), NPT = 2 * NDB * NT;
+    tsp_bf16x8 tb[RA ? NPT : 1];
+    auto trd = [&](int j) __attribute__((always_inline)) {
+      const int st = (j / NT) / NDB, db = (j / NT) % NDB;
+      const bool is_dv = DO_DV && (NT == 1 || j % 2 == 0);
+      const int ro = st * 16 * T::ROW_BYTES + (db / TP) * 256;
+      const uint8_t* base = is_dv ? ds : qs;
+      return tsp_tr_read8(base + tlo[db % TP] + ro, base + thi[db % TP] + ro);
+    };
+    if constexpr (RA) {
+#pragma unroll
+      for (int j = 0; j < RAW; ++j) tb[j] = trd(j);
+    }
     float pw[16], dsw[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -412,6 +454,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
     if constexpr (DO_DK) {
       dsf[0] = tsp_pack8(dsw);
       dsf[1] = tsp_pack8(dsw + 8);
+    }
+    if constexpr (RA) {
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        if (j + RAW < NPT) tb[j + RAW] = trd(j + RAW);
+        const int st = (j / NT) / NDB, db = (j / NT) % NDB;
+        if (DO_DV && (NT == 1 || j % 2 == 0)) dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[j], pf[st], dv[db], 0, 0, 0);
+        else dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[j], dsf[st], dk[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
     }
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -527,6 +580,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dq_bf16_kernel(TspBwdPa
   constexpr int NDB = DH / 32, NKK = DH / 16, PD = NBUF - 1, BK = T::BK;
   constexpr int VM_STAGE = T::LPW;
   static_assert(VM_STAGE * (PD - 1) < 64, "vmcnt range");
+  // RA (one wave per SIMD): every LDS operand read RAW products ahead of its product, held
+  // by scheduling barriers (the compiler's order waited the full LDS latency per product)
+  constexpr bool RA = OCC == 1 && TSP_BWD_READ_AHEAD;
+  constexpr int RAW = 4;
   const TspParams& p = bp.f;
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * T::STAGE_BYTES];
@@ -651,15 +708,41 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dq_bf16_kernel(TspBwdPa
         sT[e] = 0.f;
         dpT[e] = 0.f;
       }
+      // the transposed K operands of the dQ products: with RA the first RAW are read ahead of
+      // the weights
+      tsp_bf16x8 tb[RA ? 2 * NDB : 1];
+      auto trd = [&](int j) __attribute__((always_inline)) {  // product j: (st, db) = (j / NDB, j % NDB)
+        const int ro = (j / NDB) * 16 * T::ROW_BYTES;
+        return tsp_tr_read8(st8 + tlo[j % NDB] + ro, st8 + thi[j % NDB] + ro);
+      };
+      if constexpr (RA) {  // S^T then dP^T operands, each read RAW products ahead
+        tsp_bf16x8 ra[2 * NKK];
+        auto rd = [&](int j) __attribute__((always_inline)) {
+          return __builtin_bit_cast(tsp_bf16x8,
+                                    *reinterpret_cast<const tsp_u32x4*>(st8 + (j < NKK ? koff[j] : voff[j - NKK])));
+        };
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const tsp_bf16x8 ka = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(st8 + koff[kk]));
-        sT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sT, 0, 0, 0);
-      }
+        for (int j = 0; j < RAW; ++j) ra[j] = rd(j);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const tsp_bf16x8 va = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(st8 + voff[kk]));
-        dpT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[kk], dpT, 0, 0, 0);
+        for (int j = 0; j < 2 * NKK; ++j) {
+          if (j + RAW < 2 * NKK) ra[j + RAW] = rd(j + RAW);
+          if (j < NKK) sT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[j], qf[j], sT, 0, 0, 0);
+          else dpT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[j], dof[j - NKK], dpT, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < RAW; ++j) tb[j] = trd(j);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const tsp_bf16x8 ka = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(st8 + koff[kk]));
+          sT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sT, 0, 0, 0);
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const tsp_bf16x8 va = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(st8 + voff[kk]));
+          dpT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dof[kk], dpT, 0, 0, 0);
+        }
       }
       float dsw[16];
       const int32_t hi = qpos - t * BK - 4 * half;  // key offset limit of this lane
@@ -674,6 +757,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dq_bf16_kernel(TspBwdPa
       tsp_bf16x8 dsf[2];
       dsf[0] = tsp_pack8(dsw);
       dsf[1] = tsp_pack8(dsw + 8);
+      if constexpr (RA) {
+#pragma unroll
+        for (int j = 0; j < 2 * NDB; ++j) {
+          if (j + RAW < 2 * NDB) tb[j + RAW] = trd(j + RAW);
+          acc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[j], dsf[j / NDB], acc[j % NDB], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+      }
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
