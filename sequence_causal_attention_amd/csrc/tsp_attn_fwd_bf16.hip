@@ -68,11 +68,21 @@ KernelShape shape_of() {
   return KernelShape{tsp::Bf16Stage<DH, C::NW, C::NBUF, C::SPS>::BK, C::NW, C::RB};
 }
 
-template <int DH, int NR>
+template <int DH, int NR, typename C = Bf16Cfg<DH, NR>>
 void launch(const TspParams& p, hipStream_t stream) {
-  using C = Bf16Cfg<DH, NR>;
   hipLaunchKernelGGL((tsp::attn_fwd_bf16_kernel<DH, C::NW, C::RB, C::NBUF, C::SPS, C::OCC, NR>), dim3(p.n_units),
                      dim3(C::NW * 64), 0, stream, p);
+}
+
+// dh 128, one key range: the one-wave form pays off over long sweeps; a range shorter
+// than this (a gathered chunk, say) runs faster in the two-wave form, whose prologue,
+// epilogue and masked steps cost less.
+#ifndef TSP_DH128_ONE_WAVE_MIN_KEYS
+#define TSP_DH128_ONE_WAVE_MIN_KEYS 8192
+#endif
+void launch_dh128_one_range(const TspParams& p, hipStream_t stream) {
+  if ((int64_t)p.kv_hi - p.kv_lo >= TSP_DH128_ONE_WAVE_MIN_KEYS) launch<128, 1>(p, stream);
+  else launch<128, 1, CfgWave2>(p, stream);
 }
 
 }  // namespace
@@ -92,7 +102,7 @@ bool launch_fwd_bf16(const TspParams& p, int64_t dh, hipStream_t stream) {
   const bool two = p.kv_hi2 > p.kv_lo2;  // two key ranges in one sweep
   switch (dh) {
     case 64: two ? launch<64, 2>(p, stream) : launch<64, 1>(p, stream); return true;
-    case 128: two ? launch<128, 2>(p, stream) : launch<128, 1>(p, stream); return true;
+    case 128: two ? launch<128, 2>(p, stream) : launch_dh128_one_range(p, stream); return true;
     case 256: two ? launch<256, 2>(p, stream) : launch<256, 1>(p, stream); return true;
   }
   return false;
