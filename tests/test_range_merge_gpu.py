@@ -71,6 +71,11 @@ RANGE_CASES = [  # (B, S_total, D, rank, Hq, Hkv, dh, dtype, kv_begin, kv_end)
     # the running-max update must leave the empty rows at zero
     (1, 512, 4, 0, 4, 1, 64, torch.float32, 33, 95),
     (1, 1024, 2, 0, 8, 2, 64, torch.bfloat16, 45, 46),
+    # dh 128: ranges shorter than 8192 keys run the two-wave kernel, longer ones the
+    # one-wave kernel; both sides of that switch, and a long unaligned range
+    (1, 16384, 8, 6, 2, 2, 128, torch.bfloat16, 0, 8191),
+    (1, 16384, 8, 6, 2, 2, 128, torch.bfloat16, 0, 8192),
+    (1, 16384, 8, 1, 2, 2, 128, torch.bfloat16, 3000, 16000),
 ]
 
 
