@@ -291,11 +291,14 @@ def merge_partials(out_a, lse_a, out_b, lse_b):
 # e sequence parallelism", section 01: row-parallel pieces sum partial results). The
 # query heads that share a KV head add their contributions to it.
 # --------------------------------------------------------------------------------------
-def causal_attention_backward(q, k, v, dout, D: int, rank: int, kv_heads=None, block: int = 256):
+def causal_attention_backward(q, k, v, dout, D: int, rank: int, kv_heads=None, block: int = 256, rows=None):
     """Oracle backward for one rank.
 
     q, dout: [B, S_local, Hq, dh]; k, v: [B, S_total, Hkv, dh].
     kv_heads: optional subset of KV heads; the query heads of their groups are included.
+    rows: optional local row indices; only their terms are computed (dq of the other rows
+    stays 0, and dk / dv hold these rows' contributions, which add up over the rows, so the
+    results of a partition of the rows sum to the full result).
     Returns (dq [B, S_local, n_q, dh], dk [B, S_total, n_kv, dh], dv [B, S_total, n_kv, dh])
     in float64, n_kv = len(kv_heads), n_q = n_kv * Hq / Hkv (query heads in group order).
     Keys that no local row sees get dk = dv = 0.
@@ -307,6 +310,9 @@ def causal_attention_backward(q, k, v, dout, D: int, rank: int, kv_heads=None, b
     if S_local != pos_all.shape[0] or dout.shape != q.shape:
         raise ValueError("q_local and dout must hold 2 * S_total / (2D) rows")
     kv_heads = list(range(Hkv)) if kv_heads is None else list(kv_heads)
+    sel = np.arange(S_local) if rows is None else np.asarray(rows, dtype=np.int64)
+    if sel.size and (sel.min() < 0 or sel.max() >= S_local):
+        raise ValueError("rows outside the local rows")
     grp = Hq // Hkv
     scale = softmax_scale(dh)
     dq = np.zeros((B, S_local, len(kv_heads) * grp, dh))
@@ -319,8 +325,8 @@ def causal_attention_backward(q, k, v, dout, D: int, rank: int, kv_heads=None, b
                 h = hk * grp + g
                 if kv_head_of(h, Hq, Hkv) != hk:
                     raise ValueError("query head outside the KV head's group")
-                for start in range(0, S_local, block):
-                    r = np.arange(start, min(start + block, S_local))
+                for start in range(0, len(sel), block):
+                    r = sel[start:start + block]
                     p = pos_all[r]
                     nkeys = int(p.max()) + 1
                     keys = np.arange(nkeys, dtype=np.int64)

@@ -435,6 +435,25 @@ def pin_bwd_gqa_and_subset(o):
     assert np.array_equal(sv, dv[:, :, 1:2])
 
 
+def pin_bwd_row_subsets(o):
+    """The backward restricted to a set of local rows: over a partition of the rows (an
+    interleaved one, with a block size that splits runs), dk and dv add up to the full
+    result, each part's dq equals the full dq on its rows and is 0 elsewhere."""
+    B, S, D, r, Hq, Hkv, dh = 2, 40, 2, 1, 4, 2, 4
+    q, k, v, dout = _bwd_inputs((B, S, D, r, Hq, Hkv, dh), 85)
+    fq, fk, fv = o.causal_attention_backward(q, k, v, dout, D, r)
+    rows = np.arange(q.shape[1])
+    parts = [rows[rows % 3 == 0], rows[rows % 3 != 0][::-1]]
+    gq, gk, gv = np.zeros_like(fq), np.zeros_like(fk), np.zeros_like(fv)
+    for sel in parts:
+        dq, dk, dv = o.causal_attention_backward(q, k, v, dout, D, r, block=4, rows=sel)
+        rest = np.setdiff1d(rows, sel)
+        assert np.allclose(dq[:, sel], fq[:, sel], rtol=0, atol=1e-12) and np.all(dq[:, rest] == 0)
+        gq, gk, gv = gq + dq, gk + dk, gv + dv
+    assert np.allclose(gq, fq, rtol=0, atol=1e-12)
+    assert np.allclose(gk, fk, rtol=0, atol=1e-12) and np.allclose(gv, fv, rtol=0, atol=1e-12)
+
+
 # -- the Ulysses layout changes ---------------------------------------------------------
 
 def _coded(shape):
@@ -568,6 +587,7 @@ ALL_PINS = [
     pin_bwd_rank_partition,
     pin_bwd_closed_forms,
     pin_bwd_gqa_and_subset,
+    pin_bwd_row_subsets,
     pin_ulysses_pack_elementwise,
     pin_ulysses_round_trip_and_heads,
     pin_layer_unsharded,

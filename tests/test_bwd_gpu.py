@@ -104,6 +104,33 @@ def test_bwd_workload_sampled_heads():
     check_grad("dv", _np(dv[:, :, heads]), rv, 2)
 
 
+def test_bwd_gqa_full_size_one_query_head():
+    """The GQA dh-256 shard at full size (16384 local rows, 65536 keys, rank 2 of 4), dout
+    zero on every query head but head 7 (the second of KV head 1's group). Every other
+    head's dS is then 0, so head 7's dq (every row) and KV head 1's dk and dv (every key)
+    are the gradients of a one-head problem, which the oracle computes in full; the other
+    query heads' dq and the other KV heads' dk and dv must be exactly 0."""
+    w = workloads.BY_NAME["gqa_shard_s64k"]
+    r = w.ranks[0]
+    grp = w.Hq // w.Hkv
+    h, hk = grp + 1, 1
+    _note(f"bwd one query head {w.name} head {h}")
+    q, k, v = workloads.make_inputs(w, r)
+    dout = workloads.make_grad(q.shape, 96, torch.bfloat16)
+    keep = torch.zeros(w.Hq, dtype=torch.bool)
+    keep[h] = True
+    dout[:, :, ~keep] = 0
+    dq, dk, dv, _ = run_bwd(q, k, v, dout, w.D, r)
+    others = [x for x in range(w.Hkv) if x != hk]
+    assert (dq[:, :, ~keep.to(DEV)] == 0).all()
+    assert (dk[:, :, others] == 0).all() and (dv[:, :, others] == 0).all()
+    rq, rk, rv = oracle.causal_attention_backward(q[:, :, [h]], k[:, :, [hk]], v[:, :, [hk]], dout[:, :, [h]], w.D, r)
+    wq = check_grad("dq", _np(dq[:, :, [h]]), rq, 2)
+    wk = check_grad("dk", _np(dk[:, :, [hk]]), rk, 2)
+    wv = check_grad("dv", _np(dv[:, :, [hk]]), rv, 2)
+    _note(f"worst scaled max-abs / relative errors: dq {wq}, dk {wk}, dv {wv}")
+
+
 @pytest.mark.parametrize("name", ["gqa_shard_s64k", "ulysses_head_subset_s128k", "tsp_7b_shard_s32k"])
 def test_bwd_closed_form_sums_full_size(name):
     """At full size, for every KV head: dK sums to 0 over the keys and dV sums to the

@@ -6,7 +6,7 @@ base-2 lse, a dropped normalisation, swapped K/V operands, local instead of glob
 positions, a block-boundary error in the blocked form, or a FLOP count with one product
 per pair or without the causal mask; and, for the backward, a dropped
 softmax-Jacobian term, an unscaled dQ, a wrong operand or an overwritten GQA sum in dK,
-unnormalised weights in dV, or a strict diagonal.
+unnormalised weights in dV, a strict diagonal, or a row selection that is ignored.
 """
 
 import types
@@ -168,12 +168,13 @@ def test_blocked_form_error_is_caught():
 def _bwd_mutant(kind):
     """A copy of the oracle's backward with one plausible mistake."""
 
-    def bwd(q, k, v, dout, D, rank, kv_heads=None, block=256):
+    def bwd(q, k, v, dout, D, rank, kv_heads=None, block=256, rows=None):
         q, dout, k, v = (np.asarray(x, dtype=np.float64) for x in (q, dout, k, v))
         B, S_local, Hq, dh = q.shape
         S_total, Hkv = k.shape[1], k.shape[2]
         pos_all = A.zigzag_positions(S_total, D, rank)
         kv_heads = list(range(Hkv)) if kv_heads is None else list(kv_heads)
+        sel = np.arange(S_local) if rows is None or kind == "rows_ignored" else np.asarray(rows)
         grp = Hq // Hkv
         scale = 1.0 / np.sqrt(dh)
         dq = np.zeros((B, S_local, len(kv_heads) * grp, dh))
@@ -184,8 +185,8 @@ def _bwd_mutant(kind):
                 kb, vb = k[b, :, hk, :], v[b, :, hk, :]
                 for g in range(grp):
                     h = hk * grp + g
-                    for start in range(0, S_local, block):
-                        r = np.arange(start, min(start + block, S_local))
+                    for start in range(0, len(sel), block):
+                        r = sel[start:start + block]
                         p = pos_all[r]
                         nkeys = int(p.max()) + 1
                         keys = np.arange(nkeys)
@@ -211,7 +212,8 @@ def _bwd_mutant(kind):
     return bwd
 
 
-BWD_MUTANTS = ["no_delta", "dq_unscaled", "dk_uses_dout", "gqa_overwrite", "dv_unnormalised", "strict_diagonal"]
+BWD_MUTANTS = ["no_delta", "dq_unscaled", "dk_uses_dout", "gqa_overwrite", "dv_unnormalised", "strict_diagonal",
+               "rows_ignored"]
 
 
 @pytest.mark.parametrize("kind", BWD_MUTANTS)
