@@ -255,12 +255,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
   // swizzle only changes the low 4 bits of the chunk index, so chunks 16 apart lie 256
   // bytes apart and QP (TP) offsets serve all NKK (NDB) operands.
   constexpr int QP = DH == 256 ? NKK / 2 : NKK, TP = DH == 256 ? NDB / 2 : NDB;
-  // RA (dh 256, one wave per SIMD): every LDS operand of the products read RAW products ahead
-  // of its product, in an order held by scheduling barriers. The compiler's own order read
-  // each one just before its product, so at one wave per SIMD every product waited the full
-  // LDS latency.
-  constexpr bool RA = DH == 256 && !VLDS && TSP_BWD_READ_AHEAD;
-  constexpr int RAW = 4;
+  // RA: every LDS operand of the products read RAW products ahead of its product, in an
+  // order held by scheduling barriers. The compiler's own order read each one just before its
+  // product, so at one wave per SIMD (dh 256) every product waited the full LDS latency; at
+  // two waves (the dh-128 one-launch kernel, V parked in LDS) the other wave hid only part
+  // of it. Three products ahead is what the dh-128 kernel's registers allow without a spill
+  // in its step loop.
+  constexpr bool RA = (DH == 256 && !VLDS || DH == 128 && VLDS) && TSP_BWD_READ_AHEAD;
+  constexpr int RAW = DH == 256 ? 4 : 3;
   int qoff[QP];  // row-wise A operand read: row `col`, chunk 2kk + half
 #pragma unroll
   for (int kk = 0; kk < QP; ++kk)
@@ -270,23 +272,44 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
   tsp_tr_offsets<DH>(lane, tlo, thi);
 
   // ---- this wave's share of a stage load --------------------------------------------------
+  // Wave-load q of a stage is 1 KiB of the Q tile (q < QW) or the dO tile, rows
+  // r0 + m * RSTEP with m = q mod QW and r0 the lane's row in the first one. Where a wave's
+  // loads of a tile lie less than 16 rows apart (QW <= DP; the dh-128 one-launch kernel, one
+  // load per tile) one lane offset per m serves both tiles: two registers fewer than an
+  // offset and a row per load. Otherwise (dh 256: rows 16 apart share a swizzle, but moving
+  // the row shift into the base ran 1.3% slower; dh 64: the waves do not divide a tile's
+  // loads) each load keeps its own row and offset.
   const int64_t q_row_elems = (int64_t)p.Hq * DH;
   const uint32_t q_row_bytes = (uint32_t)(q_row_elems * 2);
-  uint32_t dma_voff[T::LPW];
-  int dma_row[T::LPW];
-  bool dma_isdo[T::LPW];
-  uint32_t dma_slot[T::LPW];
+  constexpr int QW = T::WL % NW == 0 ? T::WL / NW : 1, RSTEP = NW * T::RPL;
+  constexpr int DP = RSTEP >= 16 ? 1 : 16 / RSTEP;
+  constexpr bool SHARED = T::WL % NW == 0 && QW <= DP;
+  const int r0 = wave * T::RPL + lane / T::CPR;
+  uint32_t dma_lo[SHARED ? QW : 1];  // shared form: lane offset of the row r0 + m * RSTEP
+  constexpr int LG = SHARED ? 1 : T::LPW;
+  uint32_t dma_voff[LG];  // general form: row, lane offset, tile and slot of each load
+  int dma_row[LG];
+  bool dma_isdo[LG];
+  uint32_t dma_slot[LG];
+  if constexpr (SHARED) {
 #pragma unroll
-  for (int q = 0; q < T::LPW; ++q) {
-    const int i = q * NW + wave;
-    const bool isdo = i >= T::WL;
-    const int j = isdo ? i - T::WL : i;
-    const int row = j * T::RPL + lane / T::CPR;
-    const int c = (lane % T::CPR) ^ tsp_swz_rt<T::CPR>(row);
-    dma_row[q] = row;
-    dma_isdo[q] = isdo;
-    dma_voff[q] = (uint32_t)row * q_row_bytes + (uint32_t)(c * 16);
-    dma_slot[q] = (isdo ? T::TILE_BYTES : 0) + j * 1024;
+    for (int m = 0; m < QW; ++m) {
+      const int row = r0 + m * RSTEP;
+      dma_lo[m] = (uint32_t)row * q_row_bytes + (uint32_t)(((lane % T::CPR) ^ tsp_swz_rt<T::CPR>(row)) * 16);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < T::LPW; ++q) {
+      const int i = q * NW + wave;
+      const bool isdo = i >= T::WL;
+      const int j = isdo ? i - T::WL : i;
+      const int row = j * T::RPL + lane / T::CPR;
+      const int c = (lane % T::CPR) ^ tsp_swz_rt<T::CPR>(row);
+      dma_row[q] = row;
+      dma_isdo[q] = isdo;
+      dma_voff[q] = (uint32_t)row * q_row_bytes + (uint32_t)(c * 16);
+      dma_slot[q] = (isdo ? T::TILE_BYTES : 0) + j * 1024;
+    }
   }
   const uint32_t smem_addr = __builtin_amdgcn_readfirstlane(tsp_lds_addr(smem));
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
@@ -299,11 +322,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
     const int32_t i0 = (t_first + u % tiles) * 32;
     const int32_t h = hk * p.grp + hl;
     const int64_t tbase = ((int64_t)b * p.S_local + i0) * q_row_elems + (int64_t)h * DH;
+    if constexpr (!SHARED) {
 #pragma unroll
-    for (int q = 0; q < T::LPW; ++q) {
-      const int32_t over = max(0, i0 + dma_row[q] - (p.S_local - 1));  // rows past the last
-      tsp_lds_dma16((dma_isdo[q] ? dog : qg) + tbase, dma_voff[q] - (uint32_t)over * q_row_bytes,
-                    base + dma_slot[q]);
+      for (int q = 0; q < T::LPW; ++q) {
+        const int32_t over = max(0, i0 + dma_row[q] - (p.S_local - 1));  // rows past the last
+        tsp_lds_dma16((dma_isdo[q] ? dog : qg) + tbase, dma_voff[q] - (uint32_t)over * q_row_bytes,
+                      base + dma_slot[q]);
+      }
+    } else {  // the lane offset carries the load's whole row; rows past the last read the last
+#pragma unroll
+      for (int q = 0; q < T::LPW; ++q) {
+        const int m = q % QW;
+        const bool isdo = q >= QW;
+        const int32_t over = max(0, i0 + r0 + m * RSTEP - (p.S_local - 1));  // rows past the last
+        tsp_lds_dma16((isdo ? dog : qg) + tbase, dma_lo[m] - (uint32_t)over * q_row_bytes,
+                      base + (isdo ? T::TILE_BYTES : 0) + (m * NW + wave) * 1024);
+      }
     }
     // lse (lanes 0..31) and Delta (lanes 32..63) of the tile's rows, into this wave's slot
     const int32_t ri = min(i0 + col, p.S_local - 1);
@@ -352,18 +386,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void attn_bwd_dkv_bf16_kernel(TspBwdP
       s[e] = 0.f;
       dp[e] = 0.f;
     }
-    if constexpr (RA) {  // S then dP operands, each read RAW products ahead
+    if constexpr (RA) {  // S then dP operands (and the parked V rows), each read RAW products ahead
       constexpr int NP = DO_DK ? 2 * NKK : NKK;
-      tsp_bf16x8 ra[NP];
+      tsp_bf16x8 ra[NP], rv[VLDS ? NP : 1];
       auto rd = [&](int j) __attribute__((always_inline)) {
-        return __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>((j < NKK ? qs : ds) + qo(j % NKK)));
+        ra[j] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>((j < NKK ? qs : ds) + qo(j % NKK)));
+        if constexpr (VLDS) {
+          if (j >= NKK) rv[j] = __builtin_bit_cast(tsp_bf16x8, *reinterpret_cast<const tsp_u32x4*>(vls + 1024 * (j - NKK)));
+        }
       };
 #pragma unroll
-      for (int j = 0; j < RAW; ++j) ra[j] = rd(j);
+      for (int j = 0; j < RAW; ++j) rd(j);
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
-        if (j + RAW < NP) ra[j + RAW] = rd(j + RAW);
+        if (j + RAW < NP) rd(j + RAW);
         if (j < NKK) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[j], kf[j], s, 0, 0, 0);
+        else if constexpr (VLDS) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[j], rv[j], dp, 0, 0, 0);
         else dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[j], vf[j - NKK], dp, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
