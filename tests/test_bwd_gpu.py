@@ -131,6 +131,35 @@ def test_bwd_gqa_full_size_one_query_head():
     _note(f"worst scaled max-abs / relative errors: dq {wq}, dk {wk}, dv {wv}")
 
 
+def test_bwd_ulysses_full_size_last_rows_of_one_head():
+    """The Ulysses shard at full size (D = 1, 131072 queries and keys, dh 128), dout zero
+    except on the last 4096 rows of query head 1. Every other row's dS is then 0, so the
+    gradients are those of the oracle restricted to those rows: dq of those rows, and dk
+    and dv of KV head 1 over all 131072 keys. All other dq rows and the other KV heads'
+    dk and dv must be exactly 0."""
+    w = workloads.BY_NAME["ulysses_head_subset_s128k"]
+    r = w.ranks[0]
+    h, n_rows = 1, 4096
+    hk = h // (w.Hq // w.Hkv)
+    _note(f"bwd last rows {w.name} head {h}")
+    q, k, v = workloads.make_inputs(w, r)
+    dout = workloads.make_grad(q.shape, 94, torch.bfloat16)
+    keep = torch.zeros(w.S_local, w.Hq, dtype=torch.bool)
+    keep[w.S_local - n_rows:, h] = True
+    dout[:, ~keep] = 0
+    dq, dk, dv, _ = run_bwd(q, k, v, dout, w.D, r)
+    others = [x for x in range(w.Hkv) if x != hk]
+    assert (dq[:, ~keep.to(DEV)] == 0).all()
+    assert (dk[:, :, others] == 0).all() and (dv[:, :, others] == 0).all()
+    rows = np.arange(w.S_local - n_rows, w.S_local)
+    rq, rk, rv = oracle.causal_attention_backward(q[:, :, [h]], k[:, :, [hk]], v[:, :, [hk]], dout[:, :, [h]],
+                                                  w.D, r, rows=rows)
+    wq = check_grad("dq", _np(dq[:, w.S_local - n_rows:, [h]]), rq[:, w.S_local - n_rows:], 2)
+    wk = check_grad("dk", _np(dk[:, :, [hk]]), rk, 2)
+    wv = check_grad("dv", _np(dv[:, :, [hk]]), rv, 2)
+    _note(f"worst scaled max-abs / relative errors: dq {wq}, dk {wk}, dv {wv}")
+
+
 @pytest.mark.parametrize("name", ["gqa_shard_s64k", "ulysses_head_subset_s128k", "tsp_7b_shard_s32k"])
 def test_bwd_closed_form_sums_full_size(name):
     """At full size, for every KV head: dK sums to 0 over the keys and dV sums to the
